@@ -1,0 +1,194 @@
+"""Benchmark of the NVFP4 MoE hot path on one MI355X.
+
+One step = one full MoE layer: route + permute, NVFP4 quantisation of the tokens, gate/up
+grouped GEMM with SwiGLU, requantisation, down grouped GEMM, FINALIZE.  Default workload:
+the decode layer at ~32 rows per expert (1024 tokens, 256 experts, top-8, hidden 6144,
+intermediate 2048).  Inputs are seeded synthetic data (see synth/), resident in HBM before
+the timed region.  Prints one JSON line.
+
+value = grouped-GEMM FLOPs of the step (2 * sum_e M_e * N * K over both GEMMs, real rows
+only) / step time, in TFLOPS.  The roofline object is for the dominant kernel (the gate/up
+grouped GEMM), timed with HIP events on the stream it is launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE grouped-GEMM TFLOPS + weight HBM GB/s (% roofline) at ~32 tok/expert"
+HBM_PEAK_GBPS = 8000.0
+WORKLOADS = {"layer_decode": "LAYER_DECODE", "layer_skewed": "LAYER_SKEWED", "layer_prefill": "LAYER_PREFILL",
+             "layer_tiny": "TINY"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="layer_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def make_weights(L, moe, torch):
+    """Seeded f32 weights per expert (host threads), uploaded and NVFP4-quantised on the GPU
+    by the library's own quantiser, one dynamic global scale per expert matrix."""
+    import synth
+    from concurrent.futures import ThreadPoolExecutor
+    dev = torch.device("cuda")
+    out = {}
+    for name, rows, cols, fn in (("W1", 2 * L.I, L.H, synth.layer_w1), ("W2", L.H, L.I, synth.layer_w2)):
+        q = torch.empty(L.E, rows, cols // 2, dtype=torch.uint8, device=dev)
+        sf = torch.empty(L.E, rows, cols // 16, dtype=torch.uint8, device=dev)
+        gs = torch.empty(L.E, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(moe.lib().moe_quantize_nvfp4_workspace(rows, cols), 16), dtype=torch.uint8, device=dev)
+        staging = torch.empty(rows, cols, dtype=torch.float32, device=dev)
+        with ThreadPoolExecutor(16) as ex:
+            futs = [ex.submit(fn, L, e) for e in range(min(L.E, 32))]
+            for e in range(L.E):
+                w = futs[e].result()
+                futs[e] = None
+                if e + 32 < L.E:
+                    futs.append(ex.submit(fn, L, e + 32))
+                staging.copy_(torch.from_numpy(w))
+                moe.moe_quantize_nvfp4(staging, q[e], sf[e], gs[e:e + 1], moe.MOE_GS_DYNAMIC, None, ws)
+        torch.cuda.synchronize()
+        out[name] = moe.NVFP4Tensor(q, sf, gs)
+    return out["W1"], out["W2"]
+
+
+def cpu_baseline(L, offsets, row_src, seconds):
+    """The oracle's grouped GEMMs (gate/up then down) over the routed rows of the first
+    experts, one expert at a time until `seconds` of CPU time is spent; FLOPs / time."""
+    import oracle
+    import synth
+    logits_x = synth.layer_activations(L)
+    xq = oracle.quantize_bf16(logits_x)
+    flops, spent, experts, rows_done = 0.0, 0.0, 0, 0
+    rng = np.random.default_rng(0)
+    for e in range(L.E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        w1 = oracle.quantize(synth.layer_w1(L, e))
+        w2 = oracle.quantize(synth.layer_w2(L, e))
+        off1 = np.array([0, hi - lo], np.int32)
+        act_bits = synth.bf16_bits(rng.standard_normal((hi - lo, L.I)).astype(np.float32))
+        aq = oracle.quantize_bf16(act_bits)
+        t0 = time.perf_counter()
+        oracle.grouped_gemm(xq, w1.q[None], w1.sf[None], np.array([w1.g], np.float32), off1,
+                            A_rows=row_src[lo:hi])
+        oracle.grouped_gemm(aq, w2.q[None], w2.sf[None], np.array([w2.g], np.float32), off1)
+        spent += time.perf_counter() - t0
+        flops += 2.0 * (hi - lo) * (2 * L.I * L.H + L.H * L.I)
+        experts += 1
+        rows_done += hi - lo
+        if spent >= seconds:
+            break
+    return {"value": flops / spent / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"oracle grouped GEMMs (gate/up {2 * L.I}x{L.H} then down {L.H}x{L.I}) over the "
+                      f"{rows_done} routed rows of the first {experts} experts of the same workload, "
+                      f"{spent:.1f} s of CPU time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_scaled_fp4_02_amd as moe
+    import synth
+    L = getattr(synth, WORKLOADS[args.workload])
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    t_setup = time.time()
+    W1, W2 = make_weights(L, moe, torch)
+    logits = torch.from_numpy(synth.router_logits(L)).to(dev)
+    x = torch.from_numpy(synth.layer_activations(L).view(np.int16)).to(dev).view(torch.bfloat16)
+    plan = moe.MoELayerPlan(L.T, L.E, L.k, L.H, L.I, W1, W2)
+    torch.cuda.synchronize()
+    print(f"# setup {time.time() - t_setup:.1f}s", file=sys.stderr, flush=True)
+
+    stages = ["route", "quantize_input", "gemm1", "requantize", "gemm2", "finalize"]
+    calls = [lambda: plan.route(logits), lambda: plan.quantize_input(x), plan.gemm1, plan.requantize,
+             plan.gemm2, plan.finalize]
+    for _ in range(args.warmup):
+        plan.forward(logits, x)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        evs[s][0].record(stream)
+        for i, c in enumerate(calls):
+            c()
+            evs[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    stage_us = {st: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]) * 1e3)
+                for i, st in enumerate(stages)}
+
+    off = plan.off.cpu().numpy()
+    sizes = np.diff(off)
+    active = int((sizes > 0).sum())
+    R = int(off[-1])
+    gemm1_flops = 2.0 * R * (2 * L.I) * L.H
+    gemm2_flops = 2.0 * R * L.H * L.I
+    w1_bytes = active * (2 * L.I) * (L.H // 2 + L.H // 16)
+    w2_bytes = active * L.H * (L.I // 2 + L.I // 16)
+    x_bytes = L.T * (L.H // 2 + L.H // 16)
+    act_bytes = R * L.I * 2
+    g1_alg_bytes = w1_bytes + x_bytes + act_bytes
+    g1_s = stage_us["gemm1"] * 1e-6
+    g2_s = stage_us["gemm2"] * 1e-6
+    value = (gemm1_flops + gemm2_flops) / (ms_per_step * 1e-3) / 1e12
+    weight_gbps = (w1_bytes + w2_bytes) / (g1_s + g2_s) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": L.name, "tokens": L.T, "experts": L.E, "top_k": L.k, "hidden": L.H,
+                   "intermediate": L.I, "rows_per_expert_min_median_max": [int(sizes.min()), int(np.median(sizes)),
+                                                                           int(sizes.max())],
+                   "operands": "NVFP4 (e2m1, e4m3 scale per 16, f32 global) dequantised exactly to fp16 MFMA, fp32 accumulate"},
+        "roofline": {"kernel": "grouped_gemm_kernel (gate/up + SwiGLU)", "bound": "hbm",
+                     "achieved": round(g1_alg_bytes / g1_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(g1_alg_bytes / g1_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "alg_bytes_per_launch": int(g1_alg_bytes), "avg_launch_us": round(stage_us["gemm1"], 2)},
+        "gemm_tflops": round((gemm1_flops + gemm2_flops) / (g1_s + g2_s) / 1e12, 2),
+        "weight_hbm_GBps": round(weight_gbps, 1),
+        "weight_hbm_frac": round(weight_gbps / HBM_PEAK_GBPS, 4),
+        "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(L, off, plan.row_src.cpu().numpy(), args.cpu_baseline_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,295 @@
+"""Python binding of libmoe_nvfp4 (the MI355X NVFP4 MoE hot path).
+
+Argument marshalling only: every function here passes device pointers of torch tensors
+and torch's current HIP stream to the C ABI declared in ``include/moe_nvfp4.h`` and
+raises :class:`MoeError` on a non-zero status.  Every step of the path runs in the
+library's gfx950 kernels; there is no fallback.  If the library has not been built the
+import of any entry point fails loudly.
+
+Functions with the C names take caller-allocated tensors exactly like the C calls.  The
+``*_alloc`` helpers and :func:`moe_layer_forward` allocate outputs and workspaces with
+torch and sequence the calls of one MoE layer.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_nvfp4.so")
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
+MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
+MOE_GS_STATIC, MOE_GS_DYNAMIC = 0, 1
+MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
+
+EXPORTED = [
+    "moe_status_string", "moe_last_hip_error",
+    "moe_route_permute_workspace", "moe_route_permute",
+    "moe_quantize_nvfp4_workspace", "moe_quantize_nvfp4",
+    "moe_grouped_gemm_nvfp4_workspace", "moe_grouped_gemm_nvfp4_amax_slots",
+    "moe_grouped_gemm_nvfp4_can_implement", "moe_grouped_gemm_nvfp4",
+    "moe_finalize",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str, hip_error: int = 0):
+        super().__init__(f"{fn}: status {status} ({msg})" + (f", hipError {hip_error}" if hip_error else ""))
+        self.status = status
+
+
+class moe_gemm_args(C.Structure):
+    _fields_ = [
+        ("A", C.c_void_p), ("A_sf", C.c_void_p), ("A_gs", C.c_void_p), ("A_rows", C.c_void_p),
+        ("rows_A", C.c_int64),
+        ("B", C.c_void_p), ("B_sf", C.c_void_p), ("B_gs", C.c_void_p),
+        ("expert_offsets", C.c_void_p),
+        ("E", C.c_int32), ("N", C.c_int32), ("K", C.c_int32),
+        ("R", C.c_int64),
+        ("epilogue", C.c_int32),
+        ("D", C.c_void_p), ("amax_out", C.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library; raises if it was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(hipcc, gfx950); there is no fallback path")
+        L = C.CDLL(LIB_PATH)
+        P, i32, i64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
+        args_p = C.POINTER(moe_gemm_args)
+        sig = {
+            "moe_status_string": (C.c_char_p, [i32]),
+            "moe_last_hip_error": (i32, []),
+            "moe_route_permute_workspace": (sz, [i32, i32, i32]),
+            "moe_route_permute": (i32, [P, i32, i32, i32, P, P, P, P, P, P, sz, P]),
+            "moe_quantize_nvfp4_workspace": (sz, [i64, i64]),
+            "moe_quantize_nvfp4": (i32, [P, i32, i64, i64, P, P, P, i32, P, i64, P, sz, P]),
+            "moe_grouped_gemm_nvfp4_workspace": (sz, [args_p]),
+            "moe_grouped_gemm_nvfp4_amax_slots": (i64, [args_p]),
+            "moe_grouped_gemm_nvfp4_can_implement": (i32, [args_p]),
+            "moe_grouped_gemm_nvfp4": (i32, [args_p, P, sz, P]),
+            "moe_finalize": (i32, [P, i64, P, P, i32, i32, i32, P, P]),
+        }
+        for name, (res, argt) in sig.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, argt
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, st: int):
+    if st != MOE_OK:
+        L = lib()
+        raise MoeError(fn, st, L.moe_status_string(st).decode(),
+                       L.moe_last_hip_error() if st == MOE_ERR_HIP else 0)
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+# ---- the C entry points ------------------------------------------------------------
+
+def moe_route_permute(logits, k, topk_ids, topk_w, expert_offsets, row_src, token_slot_row,
+                      ws, stream=None):
+    T, E = logits.shape
+    _check("moe_route_permute", lib().moe_route_permute(
+        _p(logits), T, E, k, _p(topk_ids), _p(topk_w), _p(expert_offsets), _p(row_src),
+        _p(token_slot_row), _p(ws), ws.numel(), _stream(stream)))
+
+
+def moe_quantize_nvfp4(x, q, sf, gs, gs_mode=MOE_GS_DYNAMIC, amax_in=None, ws=None, stream=None):
+    rows, cols = x.shape
+    dt = {torch.bfloat16: MOE_DTYPE_BF16, torch.float32: MOE_DTYPE_F32}[x.dtype]
+    if ws is None:
+        ws = _ws(lib().moe_quantize_nvfp4_workspace(rows, cols), x.device)
+    _check("moe_quantize_nvfp4", lib().moe_quantize_nvfp4(
+        _p(x), dt, rows, cols, _p(q), _p(sf), _p(gs), gs_mode, _p(amax_in),
+        0 if amax_in is None else amax_in.numel(), _p(ws), ws.numel(), _stream(stream)))
+
+
+def make_gemm_args(A, A_sf, A_gs, B, B_sf, B_gs, expert_offsets, R, epilogue, D=None,
+                   amax_out=None, A_rows=None) -> moe_gemm_args:
+    E, N, half_k = B.shape
+    a = moe_gemm_args()
+    a.A, a.A_sf, a.A_gs, a.A_rows = _p(A), _p(A_sf), _p(A_gs), _p(A_rows)
+    a.rows_A = A.shape[0]
+    a.B, a.B_sf, a.B_gs, a.expert_offsets = _p(B), _p(B_sf), _p(B_gs), _p(expert_offsets)
+    a.E, a.N, a.K, a.R, a.epilogue = E, N, 2 * half_k, int(R), epilogue
+    a.D, a.amax_out = _p(D), _p(amax_out)
+    return a
+
+
+def moe_grouped_gemm_nvfp4_workspace(args: moe_gemm_args) -> int:
+    return lib().moe_grouped_gemm_nvfp4_workspace(C.byref(args))
+
+
+def moe_grouped_gemm_nvfp4_amax_slots(args: moe_gemm_args) -> int:
+    return lib().moe_grouped_gemm_nvfp4_amax_slots(C.byref(args))
+
+
+def moe_grouped_gemm_nvfp4_can_implement(args: moe_gemm_args) -> int:
+    return lib().moe_grouped_gemm_nvfp4_can_implement(C.byref(args))
+
+
+def moe_grouped_gemm_nvfp4(args: moe_gemm_args, ws, stream=None):
+    _check("moe_grouped_gemm_nvfp4",
+           lib().moe_grouped_gemm_nvfp4(C.byref(args), _p(ws), ws.numel(), _stream(stream)))
+
+
+def moe_finalize(Y, topk_w, token_slot_row, out, stream=None):
+    T, k = topk_w.shape
+    H = out.shape[1]
+    _check("moe_finalize", lib().moe_finalize(
+        _p(Y), Y.shape[0], _p(topk_w), _p(token_slot_row), T, k, H, _p(out), _stream(stream)))
+
+
+# ---- allocating helpers ------------------------------------------------------------
+
+@dataclass
+class NVFP4Tensor:
+    """Device NVFP4 tensor: codes [..., C/2] u8, scales [..., C/16] u8, global scale(s) f32."""
+    q: torch.Tensor
+    sf: torch.Tensor
+    gs: torch.Tensor
+
+
+def quantize_alloc(x: torch.Tensor, gs=None, amax_in=None, stream=None) -> NVFP4Tensor:
+    rows, cols = x.shape
+    q = torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device)
+    sf = torch.empty(rows, cols // 16, dtype=torch.uint8, device=x.device)
+    mode = MOE_GS_STATIC if gs is not None else MOE_GS_DYNAMIC
+    g = gs if gs is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+    moe_quantize_nvfp4(x, q, sf, g, mode, amax_in, stream=stream)
+    return NVFP4Tensor(q, sf, g)
+
+
+def route_permute_alloc(logits: torch.Tensor, k: int, stream=None):
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_src = torch.empty(T * k, dtype=torch.int32, device=dev)
+    tsr = torch.empty(T * k, dtype=torch.int32, device=dev)
+    ws = _ws(lib().moe_route_permute_workspace(T, E, k), dev)
+    moe_route_permute(logits, k, ids, w, off, row_src, tsr, ws, stream)
+    return ids, w, off, row_src, tsr
+
+
+def grouped_gemm_alloc(A: NVFP4Tensor, B: NVFP4Tensor, expert_offsets, R, epilogue=MOE_EPI_NONE,
+                       A_rows=None, stream=None):
+    """Returns D (and the partial-maxima tensor for SWIGLU)."""
+    E, N, _ = B.q.shape
+    dev = B.q.device
+    cols = N if epilogue == MOE_EPI_NONE else N // 2
+    D = torch.empty(int(R), cols, dtype=torch.bfloat16, device=dev)
+    a = make_gemm_args(A.q, A.sf, A.gs, B.q, B.sf, B.gs, expert_offsets, R, epilogue, D, None, A_rows)
+    amax = None
+    if epilogue == MOE_EPI_SWIGLU:
+        amax = torch.empty(max(moe_grouped_gemm_nvfp4_amax_slots(a), 1), dtype=torch.float32, device=dev)
+        a.amax_out = _p(amax)
+    _check("moe_grouped_gemm_nvfp4_can_implement", moe_grouped_gemm_nvfp4_can_implement(a))
+    ws = _ws(moe_grouped_gemm_nvfp4_workspace(a), dev)
+    moe_grouped_gemm_nvfp4(a, ws, stream)
+    return (D, amax) if epilogue == MOE_EPI_SWIGLU else D
+
+
+class MoELayerPlan:
+    """Pre-allocated buffers and argument blocks for repeated forward passes of one layer
+    shape (what a serving loop or a benchmark reuses): no allocation per call."""
+
+    def __init__(self, T: int, E: int, k: int, H: int, I: int, W1: NVFP4Tensor, W2: NVFP4Tensor,
+                 device="cuda"):
+        self.T, self.E, self.k, self.H, self.I = T, E, k, H, I
+        R = T * k
+        self.R = R
+        dev = torch.device(device)
+        z = lambda *s, dt: torch.empty(*s, dtype=dt, device=dev)
+        self.ids, self.w = z(T, k, dt=torch.int32), z(T, k, dt=torch.float32)
+        self.off, self.row_src, self.tsr = z(E + 1, dt=torch.int32), z(R, dt=torch.int32), z(R, dt=torch.int32)
+        self.xq = NVFP4Tensor(z(T, H // 2, dt=torch.uint8), z(T, H // 16, dt=torch.uint8), z(1, dt=torch.float32))
+        self.act = z(R, I, dt=torch.bfloat16)
+        self.actq = NVFP4Tensor(z(R, I // 2, dt=torch.uint8), z(R, I // 16, dt=torch.uint8), z(1, dt=torch.float32))
+        self.Y = z(R, H, dt=torch.bfloat16)
+        self.out = z(T, H, dt=torch.bfloat16)
+        self.W1, self.W2 = W1, W2
+        self.args1 = make_gemm_args(self.xq.q, self.xq.sf, self.xq.gs, W1.q, W1.sf, W1.gs, self.off, R,
+                                    MOE_EPI_SWIGLU, self.act, None, self.row_src)
+        self.amax = z(max(moe_grouped_gemm_nvfp4_amax_slots(self.args1), 1), dt=torch.float32)
+        self.args1.amax_out = _p(self.amax)
+        self.args2 = make_gemm_args(self.actq.q, self.actq.sf, self.actq.gs, W2.q, W2.sf, W2.gs, self.off,
+                                    R, MOE_EPI_NONE, self.Y)
+        for a in (self.args1, self.args2):
+            _check("moe_grouped_gemm_nvfp4_can_implement", moe_grouped_gemm_nvfp4_can_implement(a))
+        L = lib()
+        self.ws_route = _ws(L.moe_route_permute_workspace(T, E, k), dev)
+        self.ws_q1 = _ws(L.moe_quantize_nvfp4_workspace(T, H), dev)
+        self.ws_q2 = _ws(L.moe_quantize_nvfp4_workspace(R, I), dev)
+        self.ws_g1 = _ws(moe_grouped_gemm_nvfp4_workspace(self.args1), dev)
+        self.ws_g2 = _ws(moe_grouped_gemm_nvfp4_workspace(self.args2), dev)
+
+    # the six calls of the layer, individually (the benchmark times them one by one)
+    def route(self, logits, stream=None):
+        moe_route_permute(logits, self.k, self.ids, self.w, self.off, self.row_src, self.tsr,
+                          self.ws_route, stream)
+
+    def quantize_input(self, x, stream=None):
+        moe_quantize_nvfp4(x, self.xq.q, self.xq.sf, self.xq.gs, MOE_GS_DYNAMIC, None, self.ws_q1, stream)
+
+    def gemm1(self, stream=None):
+        moe_grouped_gemm_nvfp4(self.args1, self.ws_g1, stream)
+
+    def requantize(self, stream=None):
+        moe_quantize_nvfp4(self.act, self.actq.q, self.actq.sf, self.actq.gs, MOE_GS_DYNAMIC, self.amax,
+                           self.ws_q2, stream)
+
+    def gemm2(self, stream=None):
+        moe_grouped_gemm_nvfp4(self.args2, self.ws_g2, stream)
+
+    def finalize(self, stream=None):
+        moe_finalize(self.Y, self.w, self.tsr, self.out, stream)
+
+    def forward(self, logits, x, stream=None):
+        self.route(logits, stream)
+        self.quantize_input(x, stream)
+        self.gemm1(stream)
+        self.requantize(stream)
+        self.gemm2(stream)
+        self.finalize(stream)
+        return self.out
+
+
+def quantize_experts(W: torch.Tensor, stream=None) -> NVFP4Tensor:
+    """NVFP4-quantise stacked expert weights W [E, rows, cols] (f32 or bf16), one dynamic
+    global scale per expert, into one contiguous [E, rows, cols/2] tensor."""
+    E, rows, cols = W.shape
+    dev = W.device
+    q = torch.empty(E, rows, cols // 2, dtype=torch.uint8, device=dev)
+    sf = torch.empty(E, rows, cols // 16, dtype=torch.uint8, device=dev)
+    gs = torch.empty(E, dtype=torch.float32, device=dev)
+    ws = _ws(lib().moe_quantize_nvfp4_workspace(rows, cols), dev)
+    for e in range(E):
+        moe_quantize_nvfp4(W[e], q[e], sf[e], gs[e:e + 1], MOE_GS_DYNAMIC, None, ws, stream)
+    return NVFP4Tensor(q, sf, gs)

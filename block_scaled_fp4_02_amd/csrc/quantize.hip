@@ -1,0 +1,171 @@
+// NVFP4 quantisation: FP4 E2M1 elements, one E4M3 scale per 16 consecutive elements of a
+// row, one FP32 global scale per tensor.  The element and scale-block layout is the one
+// the pages budget for ("Cracking the SM120 Shared Memory Ceiling", section "The Shared
+// Memory Calculation": packed 4-bit elements, one 8-bit scale per 16 along K).
+//
+// Reading of the open steps: decode-direction global scale g = amax / (6 * 448) (1 for an
+// all-zero tensor); block scale s = e4m3_rne(min(amax_b / (6 g), 448)); element code
+// sign(x) | e2m1_rne(min(|x| / (s g), 6)).  Every step is one correctly rounded binary32
+// operation in a fixed order, so the result is bit-exact against any implementation that
+// takes the same steps.  Contraction is disabled in this file for that reason.
+//
+// Two kernels: amax_kernel writes up to kAmaxParts partial maxima into the workspace;
+// quant_kernel (one thread per 16-element block) first reduces those partials itself
+// (order-free, so every workgroup sees the same g) and then quantises.  Memory-bound:
+// reads 2 (bf16) or 4 (f32) bytes and writes 0.5625 bytes per element.
+#include "common.hpp"
+
+#pragma clang fp contract(off)
+
+namespace moe {
+namespace {
+
+constexpr int kAmaxParts = 256;
+
+__device__ __forceinline__ float load_abs_max8_bf16(const uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    m = fmaxf(m, fabsf(__uint_as_float(w[i] << 16)));
+    m = fmaxf(m, fabsf(__uint_as_float(w[i] & 0xffff0000u)));
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(256) void amax_kernel(const void *__restrict__ x, int x_dtype, int64_t n,
+                                                   const float *__restrict__ amax_in, int64_t n_in,
+                                                   float *__restrict__ parts) {
+  float m = 0.f;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (amax_in != nullptr) {
+    for (int64_t i = tid; i < n_in; i += stride) m = fmaxf(m, fabsf(amax_in[i]));
+  } else if (x_dtype == MOE_DTYPE_BF16) {
+    const uint4 *xv = static_cast<const uint4 *>(x);  // 8 bf16 per load; n % 16 == 0
+    for (int64_t i = tid; i < n / 8; i += stride) m = fmaxf(m, load_abs_max8_bf16(xv[i]));
+  } else {
+    const float4 *xv = static_cast<const float4 *>(x);
+    for (int64_t i = tid; i < n / 4; i += stride) {
+      const float4 v = xv[i];
+      m = fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+    }
+  }
+  m = wave_max(m);
+  __shared__ float wm[4];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) parts[blockIdx.x] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+}
+
+// Nearest E4M3FN code to t in [0, 448], ties to the even code.
+__device__ __forceinline__ uint32_t e4m3_rne(float t) {
+  if (t < 0.015625f) return static_cast<uint32_t>(rintf(t * 512.0f));  // multiples of 2^-9
+  uint32_t u = __float_as_uint(t);
+  u += 0x7ffffu + ((u >> 20) & 1u);  // round the 23-bit mantissa to 3 bits, ties to even
+  return (u >> 20) - (120u << 3);    // rebias the exponent from 127 to 7
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  if (c < 8u) return static_cast<float>(c) * 0.001953125f;  // subnormal: c * 2^-9
+  return __uint_as_float((((c >> 3) + 120u) << 23) | ((c & 7u) << 20));
+}
+
+// E2M1 magnitude code for u in [0, 6], ties to the even code.
+__device__ __forceinline__ uint32_t e2m1_rne(float u) {
+  return static_cast<uint32_t>(u > 0.25f) + static_cast<uint32_t>(u >= 0.75f) +
+         static_cast<uint32_t>(u > 1.25f) + static_cast<uint32_t>(u >= 1.75f) +
+         static_cast<uint32_t>(u > 2.5f) + static_cast<uint32_t>(u >= 3.5f) +
+         static_cast<uint32_t>(u > 5.0f);
+}
+
+__global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, int x_dtype,
+                                                    int64_t nblk, uint8_t *__restrict__ q,
+                                                    uint8_t *__restrict__ sf, float *__restrict__ gs,
+                                                    int dynamic, const float *__restrict__ parts,
+                                                    int nparts) {
+  __shared__ float sh_g;
+  if (threadIdx.x < 64) {
+    float g;
+    if (dynamic) {
+      float m = 0.f;
+      for (int i = threadIdx.x; i < nparts; i += 64) m = fmaxf(m, parts[i]);
+      m = wave_max(m);
+      g = (m > 0.f) ? m / 2688.0f : 1.0f;  // 2688 = 6 * 448
+      if (blockIdx.x == 0 && threadIdx.x == 0) *gs = g;
+    } else {
+      g = *gs;
+    }
+    if (threadIdx.x == 0) sh_g = g;
+  }
+  __syncthreads();
+  const float g = sh_g;
+  const int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (b >= nblk) return;
+  float v[16];
+  if (x_dtype == MOE_DTYPE_BF16) {
+    const uint4 *xv = static_cast<const uint4 *>(x) + 2 * b;
+    const uint4 a = xv[0], c = xv[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    const float4 *xv = static_cast<const float4 *>(x) + 4 * b;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float4 f = xv[i];
+      v[4 * i] = f.x;
+      v[4 * i + 1] = f.y;
+      v[4 * i + 2] = f.z;
+      v[4 * i + 3] = f.w;
+    }
+  }
+  float amax_b = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) amax_b = fmaxf(amax_b, fabsf(v[i]));
+  const float six_g = 6.0f * g;
+  const float t = fminf(amax_b / six_g, 448.0f);
+  const uint32_t s = e4m3_rne(t);
+  const float sg = e4m3_value(s) * g;
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const uint32_t sign = (__float_as_uint(v[i]) >> 31) << 3;
+    const uint32_t mag = (s != 0u) ? e2m1_rne(fminf(fabsf(v[i]) / sg, 6.0f)) : 0u;
+    packed[i >> 3] |= (sign | mag) << (4 * (i & 7));
+  }
+  reinterpret_cast<uint2 *>(q)[b] = make_uint2(packed[0], packed[1]);
+  sf[b] = static_cast<uint8_t>(s);
+}
+
+}  // namespace
+
+size_t quantize_ws_bytes(int64_t, int64_t) { return kAmaxParts * sizeof(float); }
+
+hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t C, uint8_t *q,
+                           uint8_t *sf, float *gs, int gs_mode, const float *amax_in,
+                           int64_t n_amax_in, void *ws, hipStream_t stream) {
+  const int64_t n = rows * C;
+  const int64_t nblk = n / 16;
+  float *parts = static_cast<float *>(ws);
+  const int dynamic = gs_mode == MOE_GS_DYNAMIC;
+  int nparts = 0;
+  if (dynamic) {
+    const int64_t work = amax_in ? n_amax_in : n;
+    int64_t g = (work + 256 * 32 - 1) / (256 * 32);
+    nparts = static_cast<int>(g < 1 ? 1 : (g > kAmaxParts ? kAmaxParts : g));
+    hipLaunchKernelGGL(amax_kernel, dim3(nparts), dim3(256), 0, stream, x, x_dtype, n, amax_in,
+                       n_amax_in, parts);
+  }
+  if (nblk > 0 || dynamic) {
+    const int64_t grid = nblk > 0 ? (nblk + 255) / 256 : 1;  // one block still publishes g
+    hipLaunchKernelGGL(quant_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, x,
+                       x_dtype, nblk, q, sf, gs, dynamic, parts, nparts);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,197 @@
+// Top-k routing and the stable permutation of (token, slot) pairs into per-expert groups.
+//
+// The pages give 256 experts with 8 active per token and one small GEMM per expert
+// driven by a per-expert problem-size array ("Tracing the Failure: Debugging CUTLASS
+// FP4 Tile Configurations on Blackwell SM120", sections "The Broader Context" and
+// "Input Knowledge Required").  Routing is the renormalised top-k softmax; the group
+// sizes stay on the device as an exclusive prefix sum.
+//
+// Kernels (all integer work is exact, so the outputs are bit-identical run to run):
+//   topk_kernel        one wavefront per token: k rounds of a wave arg-max over the
+//                      token's logits (ties -> lower id), then the softmax of the k
+//                      winners in slot order.
+//   chunk_count_kernel one workgroup per chunk of 256 tokens: a 256-bit token bitmap
+//                      per expert in LDS (order-free OR), popcounts -> counts[chunk][e].
+//   offsets_kernel     one workgroup: per expert an exclusive scan over chunks, then
+//                      an exclusive scan over experts -> expert_offsets.
+//   scatter_kernel     one workgroup per chunk: rebuild the bitmaps; the rank of token t
+//                      in expert e's group within the chunk is the popcount of the bits
+//                      below t, which is the stable order t*k + j because a token names
+//                      each expert at most once.
+#include "common.hpp"
+
+#include <limits.h>
+
+namespace moe {
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxPerLane = kMaxE / kWave;  // logits held per lane
+constexpr int kChunk = 256;                 // tokens per permutation chunk
+constexpr int kWords = kChunk / 64;         // 64-bit bitmap words per expert
+
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
+                                                   int k, int32_t *__restrict__ topk_ids,
+                                                   float *__restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float *L = logits + static_cast<int64_t>(t) * E;
+  float v[kMaxPerLane];
+  uint32_t absent = 0;  // bit i: element lane + 64 i is taken or does not exist
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; i++) {
+    const int e = lane + kWave * i;
+    if (e < E) {
+      v[i] = L[e];
+    } else {
+      v[i] = 0.f;
+      absent |= 1u << i;
+    }
+  }
+  float my_v = 0.f;
+  int my_id = 0;
+  for (int j = 0; j < k; j++) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; i++) {
+      // ids grow with i, so a strictly larger value is needed to displace the best
+      if (!((absent >> i) & 1u) && (bi == INT_MAX || v[i] > bv)) {
+        bv = v[i];
+        bi = lane + kWave * i;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      const bool better = oi != INT_MAX && (bi == INT_MAX || ov > bv || (ov == bv && oi < bi));
+      if (better) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) absent |= 1u << (bi >> 6);
+    if (lane == j) {
+      my_v = bv;
+      my_id = bi;
+    }
+  }
+  const float v0 = __shfl(my_v, 0, kWave);
+  const float ex = (lane < k) ? expf(my_v - v0) : 0.f;
+  float denom = 0.f;
+  for (int i = 0; i < k; i++) denom += __shfl(ex, i, kWave);  // slot order, same in every lane
+  if (lane < k) {
+    topk_ids[static_cast<int64_t>(t) * k + lane] = my_id;
+    topk_w[static_cast<int64_t>(t) * k + lane] = ex / denom;
+  }
+}
+
+__device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+// Fill the chunk's per-expert token bitmaps (bm[e * kWords + w]).
+__device__ __forceinline__ void build_bitmaps(unsigned long long *bm, const int32_t *ids, int T,
+                                              int E, int k, int chunk) {
+  for (int i = threadIdx.x; i < E * kWords; i += blockDim.x) bm[i] = 0ull;
+  __syncthreads();
+  const int t = chunk * kChunk + threadIdx.x;
+  if (t < T) {
+    const unsigned long long bit = 1ull << (threadIdx.x & 63);
+    for (int j = 0; j < k; j++) {
+      const int e = clamp_expert(ids[static_cast<int64_t>(t) * k + j], E);
+      atomicOr(&bm[e * kWords + (threadIdx.x >> 6)], bit);
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kChunk) void chunk_count_kernel(const int32_t *__restrict__ ids, int T,
+                                                             int E, int k,
+                                                             int32_t *__restrict__ counts) {
+  __shared__ unsigned long long bm[kMaxE * kWords];
+  build_bitmaps(bm, ids, T, E, k, blockIdx.x);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kWords; w++) c += __popcll(bm[e * kWords + w]);
+    counts[static_cast<int64_t>(blockIdx.x) * E + e] = c;
+  }
+}
+
+__global__ __launch_bounds__(1024) void offsets_kernel(int32_t *__restrict__ counts, int nchunks,
+                                                       int E, int32_t *__restrict__ offsets) {
+  __shared__ int32_t s[1024];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; c++) {  // counts[c][e] becomes its exclusive prefix over chunks
+      const int64_t i = static_cast<int64_t>(c) * E + e;
+      const int n = counts[i];
+      counts[i] = total;
+      total += n;
+    }
+  }
+  s[e] = total;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan over experts
+    const int add = (e >= o) ? s[e - o] : 0;
+    __syncthreads();
+    s[e] += add;
+    __syncthreads();
+  }
+  if (e < E) offsets[e] = s[e] - total;
+  if (e == E - 1) offsets[E] = s[e];
+}
+
+__global__ __launch_bounds__(kChunk) void scatter_kernel(const int32_t *__restrict__ ids, int T, int E,
+                                                         int k, const int32_t *__restrict__ counts,
+                                                         const int32_t *__restrict__ offsets,
+                                                         int32_t *__restrict__ row_src,
+                                                         int32_t *__restrict__ token_slot_row) {
+  __shared__ unsigned long long bm[kMaxE * kWords];
+  build_bitmaps(bm, ids, T, E, k, blockIdx.x);
+  const int t = blockIdx.x * kChunk + threadIdx.x;
+  if (t >= T) return;
+  const int word = threadIdx.x >> 6;
+  const unsigned long long below = (1ull << (threadIdx.x & 63)) - 1ull;
+  const int64_t n = static_cast<int64_t>(T) * k;
+  for (int j = 0; j < k; j++) {
+    const int e = clamp_expert(ids[static_cast<int64_t>(t) * k + j], E);
+    int rank = __popcll(bm[e * kWords + word] & below);
+    for (int w = 0; w < word; w++) rank += __popcll(bm[e * kWords + w]);
+    int64_t p = static_cast<int64_t>(offsets[e]) + counts[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
+    p = p < 0 ? 0 : (p >= n ? n - 1 : p);
+    row_src[p] = t;
+    token_slot_row[static_cast<int64_t>(t) * k + j] = static_cast<int32_t>(p);
+  }
+}
+
+}  // namespace
+
+size_t route_permute_ws_bytes(int T, int E, int /*k*/) {
+  const int64_t nchunks = (static_cast<int64_t>(T) + kChunk - 1) / kChunk;
+  return static_cast<size_t>((nchunks > 0 ? nchunks : 1) * E * sizeof(int32_t));
+}
+
+hipError_t launch_route_permute(const float *logits, int T, int E, int k, int32_t *topk_ids,
+                                float *topk_w, int32_t *expert_offsets, int32_t *row_src,
+                                int32_t *token_slot_row, void *ws, hipStream_t stream) {
+  int32_t *counts = static_cast<int32_t *>(ws);
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  if (T > 0) {
+    hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k,
+                       topk_ids, topk_w);
+    hipLaunchKernelGGL(chunk_count_kernel, dim3(nchunks), dim3(kChunk), 0, stream, topk_ids, T, E,
+                       k, counts);
+  }
+  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, stream, counts, nchunks, E,
+                     expert_offsets);
+  if (T > 0) {
+    hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(kChunk), 0, stream, topk_ids, T, E, k,
+                       counts, expert_offsets, row_src, token_slot_row);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

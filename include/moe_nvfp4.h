@@ -1,0 +1,189 @@
+/*
+ * moe_nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 Mixture-of-Experts hot path.
+ *
+ * The path, for one MoE layer of T tokens, E experts, top-k routing, hidden H and
+ * expert intermediate I:
+ *   1. moe_route_permute   top-k routing of the router logits and the stable
+ *                          permutation of the T*k (token, slot) pairs into
+ *                          per-expert groups;
+ *   2. moe_quantize_nvfp4  NVFP4 quantisation of the bf16 token activations;
+ *   3. moe_grouped_gemm_nvfp4 (MOE_EPI_SWIGLU)  gate/up GEMM over the groups,
+ *                          gathering token rows, with SwiGLU in the epilogue;
+ *   4. moe_quantize_nvfp4  requantisation of the SwiGLU output;
+ *   5. moe_grouped_gemm_nvfp4 (MOE_EPI_NONE)  down GEMM into a bf16 workspace;
+ *   6. moe_finalize        router-weighted gather-reduce of each token's k rows
+ *                          into the bf16 output.
+ *
+ * Sources (web pages cited by title and section):
+ *  - Operands are FP4 E2M1 with one FP8 scale per 16 elements along the
+ *    contraction dimension for both operands, BF16 output: "Cracking the SM120
+ *    Shared Memory Ceiling", section "The Shared Memory Calculation"; the FP4 x
+ *    FP4 -> BF16 kernel instantiation quoted in "The CUTLASS Tile That Wouldn't
+ *    Fit: Debugging EP8 on Blackwell SM120", section "The Crash: A Deep-Dive into CUTLASS Tile Geometry".
+ *  - Many small per-expert GEMMs in one launch driven by a per-expert
+ *    problem-size array: "Tracing the Failure: Debugging CUTLASS FP4 Tile
+ *    Configurations on Blackwell SM120", section "Input Knowledge Required".
+ *  - 256 experts, 8 active per token, about 32 rows per expert at decode, GEMMs
+ *    of about 32 x 2048 x 6144: same page, section "The Broader Context".
+ *  - NONE (pass-through) and FINALIZE epilogues: "The Epilogue That Broke the
+ *    Kernel", section "The Insight: FINALIZE vs NONE".
+ *  - A truthful can-implement check, a workspace query and no exception across
+ *    the interface: the failure traced in "Cracking the SM120 Shared Memory
+ *    Ceiling", section "Tracing the Failure" (the check passed, initialisation
+ *    then failed) and the warmup exception in "The CUTLASS Tile That Wouldn't
+ *    Fit: Debugging EP8 on Blackwell SM120", section "The Crash: A Deep-Dive into CUTLASS Tile Geometry".
+ *  - E2M1 / E4M3 encodings: OCP OFP8 rev 1.0 and OCP MX v1.0.
+ *
+ * Conventions for every entry point:
+ *  - Every data pointer is a DEVICE pointer on the current HIP device, owned by
+ *    the caller; the library allocates no device memory, keeps no pointer after
+ *    it returns and holds no global state apart from a thread-local last HIP
+ *    error code.
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream); no call
+ *    synchronises with the device or copies device data to the host.
+ *  - Arguments are validated on the host before any HIP call; failures return a
+ *    status and enqueue nothing.  Nothing throws or aborts across the ABI.
+ *  - Device-data invariants (expert ids in range, monotone offsets, finite
+ *    values) are the caller's contract; indices read from device memory are
+ *    clamped so that bad values cannot make a kernel access memory out of
+ *    bounds.
+ *  - Results are deterministic: no floating-point atomics; repeated calls on the
+ *    same inputs produce identical bytes.
+ *  - Element layout of NVFP4 tensors [rows, C]: codes [rows, C/2] bytes, element
+ *    2i in the low nibble of byte i and 2i+1 in the high nibble; scales
+ *    [rows, C/16] E4M3FN bytes (bias 7, max 448); one FP32 global scale g; the
+ *    value of an element is e2m1(code) * e4m3(scale) * g.
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* a size is negative, inconsistent or out of range */
+  MOE_ERR_UNSUPPORTED = 3, /* valid but not supported by the kernels (e.g. K % 256) */
+  MOE_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than the query returned */
+  MOE_ERR_HIP = 5          /* a HIP launch failed; see moe_last_hip_error() */
+} moe_status;
+
+/* Static description of a status; never NULL. */
+const char *moe_status_string(moe_status s);
+/* hipError_t of the last MOE_ERR_HIP returned on the calling thread (0 if none). */
+int moe_last_hip_error(void);
+
+/* ---------------------------------------------------------------------------
+ * 1. Routing and permutation.
+ *
+ * logits [T, E] f32 row-major.  For each token the k largest logits are taken in
+ * descending order, equal logits going to the lower expert id:
+ *   topk_ids [T, k] i32, topk_w [T, k] f32 = softmax over the k chosen logits
+ *   (the renormalised top-k of the full softmax).
+ * The T*k pairs (t, j), in the order t*k + j, are then grouped by expert, stably:
+ *   expert_offsets [E+1] i32  exclusive prefix sum of the group sizes
+ *                             (expert_offsets[E] = T*k);
+ *   row_src [T*k] i32         token of permuted row p;
+ *   token_slot_row [T*k] i32  permuted row of pair (t, j).
+ * Limits: 0 <= T, 1 <= E <= 1024, 1 <= k <= min(E, 32), T*k < 2^31.
+ * ws: at least moe_route_permute_workspace(T, E, k) bytes of device memory
+ * (contents on entry irrelevant).
+ * ------------------------------------------------------------------------- */
+size_t moe_route_permute_workspace(int T, int E, int k);
+moe_status moe_route_permute(const float *logits, int T, int E, int k, int32_t *topk_ids,
+                             float *topk_w, int32_t *expert_offsets, int32_t *row_src,
+                             int32_t *token_slot_row, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * 2. NVFP4 quantisation of x [rows, C] (C % 16 == 0), blocks of 16 along C.
+ *
+ * x_dtype: MOE_DTYPE_BF16 (x is uint16 bf16 bit patterns) or MOE_DTYPE_F32.
+ * gs_mode MOE_GS_DYNAMIC: g = amax / 2688 in binary32 (1 if amax is 0), written
+ *   to *gs; amax is max|x| over the whole tensor, or, when amax_in is not NULL,
+ *   the maximum of the n_amax_in values amax_in[] (e.g. the partial maxima a
+ *   SwiGLU GEMM wrote).
+ * gs_mode MOE_GS_STATIC: g is read from *gs.
+ * Then per block b: t = amax_b / (6 g), s = e4m3(min(t, 448)) (round to nearest
+ * even), and per element u = |x| / (s g), code = sign(x) | e2m1(min(u, 6))
+ * (round to nearest even); a block with s = 0 holds signed zeros.  Every step
+ * is a correctly rounded binary32 operation, so the output is bit-exact.
+ * q [rows, C/2] u8, sf [rows, C/16] u8, gs: one f32.
+ * Limits: rows >= 0, C >= 16, rows*C < 2^40.  ws: moe_quantize_nvfp4_workspace().
+ * ------------------------------------------------------------------------- */
+enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 };
+enum { MOE_GS_STATIC = 0, MOE_GS_DYNAMIC = 1 };
+size_t moe_quantize_nvfp4_workspace(int64_t rows, int64_t C);
+moe_status moe_quantize_nvfp4(const void *x, int x_dtype, int64_t rows, int64_t C, uint8_t *q,
+                              uint8_t *sf, float *gs, int gs_mode, const float *amax_in,
+                              int64_t n_amax_in, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * 3. Grouped NVFP4 GEMM.
+ *
+ * For expert e and permuted row p in [expert_offsets[e], expert_offsets[e+1]):
+ *   y[p, n] = gA * gB[e] * sum_kb sA[r, kb] sB[e, n, kb] sum_{i<16} a[r, 16kb+i] b[e, n, 16kb+i]
+ * with r = A_rows ? A_rows[p] : p.  Products are exact (fp16 MFMA on operands
+ * dequantised exactly), sums are binary32.
+ *   A [rows_A, K] NVFP4 (A, A_sf, *A_gs), B [E, N, K] NVFP4 (B, B_sf, B_gs[E]),
+ *   expert_offsets [E+1] i32 on the device (group sizes are never read on the
+ *   host), R = the number of permuted rows (the row capacity of D).
+ * Epilogues:
+ *   MOE_EPI_NONE    D bf16 [R, N]: D[p, n] = bf16(y[p, n]).
+ *   MOE_EPI_SWIGLU  N = 2I; columns [0, I) are gate, [I, 2I) are up;
+ *                   D bf16 [R, I]: D[p, i] = bf16(silu(bf16(y[p, i])) * bf16(y[p, I+i]))
+ *                   with silu(x) = x / (1 + exp(-x)) in binary32, and
+ *                   amax_out[moe_grouped_gemm_nvfp4_amax_slots(args)] f32 receives
+ *                   partial maxima of |D| (their maximum is max|D|; unused slots 0),
+ *                   for moe_quantize_nvfp4(..., amax_in = amax_out, ...).
+ * Rows p >= expert_offsets[E] of D are not written.
+ * Supported: K % 256 == 0, N % 256 == 0, 1 <= E <= 65536, 0 <= R < 2^31.
+ * moe_grouped_gemm_nvfp4_can_implement() returns MOE_OK exactly when the
+ * launch is supported; a supported launch then cannot fail on its
+ * configuration.  ws: moe_grouped_gemm_nvfp4_workspace(args) bytes.
+ * ------------------------------------------------------------------------- */
+typedef enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1 } moe_epilogue;
+
+typedef struct moe_gemm_args {
+  const uint8_t *A;               /* [rows_A, K/2] */
+  const uint8_t *A_sf;            /* [rows_A, K/16] */
+  const float *A_gs;              /* one f32 */
+  const int32_t *A_rows;          /* [R] gather map, or NULL for the identity */
+  int64_t rows_A;                 /* rows of A */
+  const uint8_t *B;               /* [E, N, K/2] */
+  const uint8_t *B_sf;            /* [E, N, K/16] */
+  const float *B_gs;              /* [E] */
+  const int32_t *expert_offsets;  /* [E+1] */
+  int32_t E, N, K;
+  int64_t R;
+  int32_t epilogue;               /* moe_epilogue */
+  void *D;                        /* bf16 [R, N] (NONE) or [R, N/2] (SWIGLU) */
+  float *amax_out;                /* SWIGLU only */
+} moe_gemm_args;
+
+size_t moe_grouped_gemm_nvfp4_workspace(const moe_gemm_args *args);
+int64_t moe_grouped_gemm_nvfp4_amax_slots(const moe_gemm_args *args);
+moe_status moe_grouped_gemm_nvfp4_can_implement(const moe_gemm_args *args);
+moe_status moe_grouped_gemm_nvfp4(const moe_gemm_args *args, void *ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * 4. FINALIZE: out[t, h] = bf16(sum_{j<k} topk_w[t, j] * Y[token_slot_row[t*k+j], h]),
+ * summed in binary32 in slot order (a per-token gather-reduce: no atomics,
+ * deterministic).  Y bf16 [R, H], topk_w f32 [T, k], token_slot_row i32 [T*k],
+ * out bf16 [T, H].  Limits: T >= 0, 1 <= k <= 32, H % 8 == 0, H >= 8.
+ * ------------------------------------------------------------------------- */
+moe_status moe_finalize(const uint16_t *Y, int64_t R, const float *topk_w,
+                        const int32_t *token_slot_row, int T, int k, int H, uint16_t *out,
+                        hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_NVFP4_H */

@@ -20,7 +20,7 @@ _lib = None
 
 def build() -> str:
     """Compile liboracle.so with gcc (plain C11, OpenMP, no FP contraction)."""
-    cmd = ["gcc", "-std=c11", "-O2", "-march=x86-64-v2", "-ffp-contract=off", "-fno-fast-math",
+    cmd = ["gcc", "-std=c11", "-O3", "-march=x86-64-v3", "-ffp-contract=off", "-fno-fast-math",
            "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
            os.path.join(_HERE, "oracle.c"), "-o", _LIB_PATH + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)

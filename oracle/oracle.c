@@ -35,10 +35,14 @@ double orc_e4m3_value(int code) {
 /* Magnitude tables, filled from the decode functions above when the library
  * is loaded. */
 static double e4m3_mag[127], e2m1_mag[8];
+static double e4m3_all[256];   /* value of every E4M3 code */
+static int e2m1_twice_all[16]; /* twice the value of every E2M1 code: an integer */
 
 __attribute__((constructor)) static void fill_tables(void) {
   for (int c = 0; c < 127; c++) e4m3_mag[c] = orc_e4m3_value(c);
   for (int c = 0; c < 8; c++) e2m1_mag[c] = orc_e2m1_value(c);
+  for (int c = 0; c < 256; c++) e4m3_all[c] = orc_e4m3_value(c);
+  for (int c = 0; c < 16; c++) e2m1_twice_all[c] = (int)(2.0 * orc_e2m1_value(c));
 }
 
 /* Nearest of the increasing magnitudes mag[0..n-1] to x >= 0, ties to the even
@@ -196,16 +200,21 @@ void orc_permute(const int32_t *topk_ids, int T, int E, int k,
 
 /* ---- grouped GEMM ---- */
 
-/* Twice the E2M1 value of a code, an exact integer in [-12, 12]. */
-static int e2m1_twice(int code) { return (int)(2.0 * orc_e2m1_value(code)); }
+/* Sum over one 16-element block of the products of doubled E2M1 values: an exact
+ * integer, |P| <= 16 * 12 * 12 = 2304. */
+static inline int block_dot(const int16_t *a, const int16_t *b) {
+  int P = 0;
+  for (int i = 0; i < 16; i++) P += a[i] * b[i];
+  return P;
+}
 
 /* Decode one NVFP4 row of K elements into doubled integer values and FP64 block scales. */
-static void decode_row(const uint8_t *q, const uint8_t *sf, int K, int8_t *v2, double *s) {
+static void decode_row(const uint8_t *q, const uint8_t *sf, int K, int16_t *v2, double *s) {
   for (int c = 0; c < K; c++) {
     uint8_t byte = q[c / 2];
-    v2[c] = (int8_t)e2m1_twice((c & 1) ? (byte >> 4) : (byte & 15));
+    v2[c] = (int16_t)e2m1_twice_all[(c & 1) ? (byte >> 4) : (byte & 15)];
   }
-  for (int b = 0; b < K / 16; b++) s[b] = orc_e4m3_value(sf[b]);
+  for (int b = 0; b < K / 16; b++) s[b] = e4m3_all[sf[b]];
 }
 
 void orc_grouped_gemm_rows(const uint8_t *A, const uint8_t *A_sf, float gA,
@@ -214,50 +223,51 @@ void orc_grouped_gemm_rows(const uint8_t *A, const uint8_t *A_sf, float gA,
                            const int32_t *expert_offsets, int E, int N, int K,
                            const int32_t *rows, int64_t nrows, double *y) {
   const int nkb = K / 16;
-  int8_t *bv = (int8_t *)malloc((size_t)N * K);
-  double *bs = (double *)malloc((size_t)N * nkb * sizeof(double));
   int64_t *mine = (int64_t *)malloc((size_t)(nrows > 0 ? nrows : 1) * sizeof(int64_t));
+  int16_t *av = (int16_t *)malloc((size_t)(nrows > 0 ? nrows : 1) * K * sizeof(int16_t));
+  double *as = (double *)malloc((size_t)(nrows > 0 ? nrows : 1) * nkb * sizeof(double));
   for (int e = 0; e < E; e++) {
+    /* the requested rows that belong to expert e, decoded once */
     int64_t cnt = 0;
     for (int64_t i = 0; i < nrows; i++)
       if (rows[i] >= expert_offsets[e] && rows[i] < expert_offsets[e + 1]) mine[cnt++] = i;
     if (cnt == 0) continue;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < cnt; i++) {
+      int64_t p = rows[mine[i]];
+      int64_t r = A_rows ? A_rows[p] : p;
+      decode_row(A + r * (K / 2), A_sf + r * nkb, K, av + i * K, as + i * nkb);
+    }
     const uint8_t *Be = B + (int64_t)e * N * (K / 2);
     const uint8_t *Bse = B_sf + (int64_t)e * N * nkb;
-#pragma omp parallel for schedule(static)
-    for (int n = 0; n < N; n++)
-      decode_row(Be + (int64_t)n * (K / 2), Bse + (int64_t)n * nkb, K,
-                 bv + (int64_t)n * K, bs + (int64_t)n * nkb);
     const double gscale = (double)gA * (double)gB[e];
+    /* every output y[p, n] is computed by the same sequence of operations; the loops
+     * only choose the order in which independent outputs are produced */
 #pragma omp parallel
     {
-      int8_t *av = (int8_t *)malloc((size_t)K);
-      double *as = (double *)malloc((size_t)nkb * sizeof(double));
-#pragma omp for schedule(dynamic, 1)
-      for (int64_t i = 0; i < cnt; i++) {
-        int64_t p = rows[mine[i]];
-        int64_t r = A_rows ? A_rows[p] : p;
-        decode_row(A + r * (K / 2), A_sf + r * nkb, K, av, as);
-        double *yrow = y + mine[i] * (int64_t)N;
-        for (int n = 0; n < N; n++) {
-          const int8_t *b = bv + (int64_t)n * K;
-          const double *sb = bs + (int64_t)n * nkb;
+      int16_t *bv = (int16_t *)malloc((size_t)K * sizeof(int16_t));
+      double *bs = (double *)malloc((size_t)nkb * sizeof(double));
+#pragma omp for schedule(static)
+      for (int n = 0; n < N; n++) {
+        decode_row(Be + (int64_t)n * (K / 2), Bse + (int64_t)n * nkb, K, bv, bs);
+        for (int64_t i = 0; i < cnt; i++) {
+          const int16_t *a = av + i * K;
+          const double *sa = as + i * nkb;
           double acc = 0.0;
           for (int kb = 0; kb < nkb; kb++) {
-            int P = 0; /* (2a)(2b) summed over the block: exact, |P| <= 2304 */
-            for (int i2 = 0; i2 < 16; i2++) P += (int)av[kb * 16 + i2] * (int)b[kb * 16 + i2];
-            acc += (double)P * as[kb] * sb[kb] * 0.25;
+            int P = block_dot(a + kb * 16, bv + kb * 16);
+            acc += (double)P * sa[kb] * bs[kb] * 0.25;
           }
-          yrow[n] = acc * gscale;
+          y[mine[i] * (int64_t)N + n] = acc * gscale;
         }
       }
-      free(av);
-      free(as);
+      free(bv);
+      free(bs);
     }
   }
-  free(bv);
-  free(bs);
   free(mine);
+  free(av);
+  free(as);
 }
 
 /* ---- SwiGLU and FINALIZE ---- */

@@ -1,0 +1,133 @@
+"""The C ABI on the CPU: the library loads, exports every function include/moe_nvfp4.h
+declares, and every host-side validation returns its documented status before any HIP
+call (no GPU needed: invalid calls never reach a launch)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_02_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_nvfp4.h")
+FAKE = C.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(moe_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 11
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(moe.EXPORTED) == names
+
+
+def test_status_strings():
+    L = moe.lib()
+    for s in range(7):
+        assert L.moe_status_string(s)
+    assert L.moe_last_hip_error() == 0
+
+
+def test_route_permute_validation():
+    L = moe.lib()
+    ws = L.moe_route_permute_workspace(16, 4, 2)
+    assert ws > 0
+    args = lambda T, E, k, logits=FAKE, ws_bytes=ws: (logits, T, E, k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+    assert L.moe_route_permute(*args(16, 4, 2, logits=None)) == moe.MOE_ERR_NULL
+    assert L.moe_route_permute(*args(-1, 4, 2)) == moe.MOE_ERR_SHAPE
+    assert L.moe_route_permute(*args(16, 4, 5)) == moe.MOE_ERR_SHAPE      # k > E
+    assert L.moe_route_permute(*args(16, 4, 0)) == moe.MOE_ERR_SHAPE
+    assert L.moe_route_permute(*args(16, 2048, 2)) == moe.MOE_ERR_SHAPE   # E > 1024
+    assert L.moe_route_permute(*args(16, 64, 33)) == moe.MOE_ERR_SHAPE    # k > 32
+    assert L.moe_route_permute(*args(16, 4, 2, ws_bytes=ws - 1)) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_route_permute_workspace(-1, 4, 2) == 0
+
+
+def test_quantize_validation():
+    L = moe.lib()
+    ws = L.moe_quantize_nvfp4_workspace(4, 32)
+    q = lambda rows, cols, x=FAKE, dtype=0, mode=1, gs=FAKE, ws_bytes=ws: L.moe_quantize_nvfp4(
+        x, dtype, rows, cols, FAKE, FAKE, gs, mode, None, 0, FAKE, ws_bytes, None)
+    assert q(4, 24) == moe.MOE_ERR_SHAPE           # C % 16
+    assert q(4, 8) == moe.MOE_ERR_SHAPE
+    assert q(-1, 32) == moe.MOE_ERR_SHAPE
+    assert q(4, 32, x=None) == moe.MOE_ERR_NULL
+    assert q(4, 32, gs=None) == moe.MOE_ERR_NULL
+    assert q(4, 32, dtype=7) == moe.MOE_ERR_UNSUPPORTED
+    assert q(4, 32, mode=9) == moe.MOE_ERR_UNSUPPORTED
+    assert q(4, 32, ws_bytes=0) == moe.MOE_ERR_WORKSPACE
+
+
+def gemm_args(E=8, N=2048, K=6144, R=256, epi=0, null=None):
+    a = moe.moe_gemm_args()
+    for f in ("A", "A_sf", "A_gs", "B", "B_sf", "B_gs", "expert_offsets", "D", "amax_out"):
+        setattr(a, f, FAKE)
+    a.rows_A, a.E, a.N, a.K, a.R, a.epilogue = R, E, N, K, R, epi
+    if null:
+        setattr(a, null, None)
+    return a
+
+
+def test_gemm_can_implement_is_truthful_on_shapes():
+    L = moe.lib()
+    ok = gemm_args()
+    assert L.moe_grouped_gemm_nvfp4_can_implement(C.byref(ok)) == moe.MOE_OK
+    assert L.moe_grouped_gemm_nvfp4_workspace(C.byref(ok)) > 0
+    assert L.moe_grouped_gemm_nvfp4_amax_slots(C.byref(ok)) > 0
+    cases = [
+        (dict(K=100), moe.MOE_ERR_SHAPE),           # K % 16
+        (dict(K=272), moe.MOE_ERR_UNSUPPORTED),     # K % 256
+        (dict(N=100), moe.MOE_ERR_UNSUPPORTED),     # N % 256
+        (dict(E=0), moe.MOE_ERR_SHAPE),
+        (dict(R=-1), moe.MOE_ERR_SHAPE),
+        (dict(epi=5), moe.MOE_ERR_UNSUPPORTED),
+        (dict(null="B"), moe.MOE_ERR_NULL),
+        (dict(null="expert_offsets"), moe.MOE_ERR_NULL),
+        (dict(null="D"), moe.MOE_ERR_NULL),
+        (dict(epi=1, null="amax_out"), moe.MOE_ERR_NULL),
+    ]
+    for kw, want in cases:
+        a = gemm_args(**kw)
+        assert L.moe_grouped_gemm_nvfp4_can_implement(C.byref(a)) == want, kw
+        assert L.moe_grouped_gemm_nvfp4(C.byref(a), FAKE, 1 << 30, None) == want, kw
+    assert L.moe_grouped_gemm_nvfp4_can_implement(None) == moe.MOE_ERR_NULL
+    # amax_out is only needed by the SwiGLU epilogue
+    assert L.moe_grouped_gemm_nvfp4_can_implement(C.byref(gemm_args(null="amax_out"))) == moe.MOE_OK
+    # a short workspace is refused before any launch
+    ws = L.moe_grouped_gemm_nvfp4_workspace(C.byref(ok))
+    assert L.moe_grouped_gemm_nvfp4(C.byref(ok), FAKE, ws - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_grouped_gemm_nvfp4(C.byref(ok), None, ws, None) == moe.MOE_ERR_WORKSPACE
+
+
+def test_gemm_workspace_grows_with_rows_and_experts():
+    L = moe.lib()
+    small = L.moe_grouped_gemm_nvfp4_workspace(C.byref(gemm_args(E=8, R=256)))
+    big = L.moe_grouped_gemm_nvfp4_workspace(C.byref(gemm_args(E=256, R=131072)))
+    assert big > small > 0
+
+
+def test_finalize_validation():
+    L = moe.lib()
+    f = lambda T, k, H, R=64, Y=FAKE: L.moe_finalize(Y, R, FAKE, FAKE, T, k, H, FAKE, None)
+    assert f(8, 2, 12) == moe.MOE_ERR_UNSUPPORTED     # H % 8
+    assert f(8, 0, 64) == moe.MOE_ERR_SHAPE
+    assert f(8, 33, 64) == moe.MOE_ERR_SHAPE
+    assert f(-1, 2, 64) == moe.MOE_ERR_SHAPE
+    assert f(8, 2, 64, R=0) == moe.MOE_ERR_SHAPE
+    assert f(8, 2, 64, Y=None) == moe.MOE_ERR_NULL
+
+
+def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(moe, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        moe.lib()

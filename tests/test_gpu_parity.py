@@ -1,0 +1,388 @@
+"""GPU parity: every entry point of libmoe_nvfp4, called through the C ABI, against the CPU
+oracle on the same seeded inputs (oracle-side inputs are uploaded to the GPU; nothing the
+GPU computes is ever fed to the oracle).
+
+Sizes: the small cases span several tiles and ragged tails; the full-size cases use the
+decode layer (1024 tokens, 256 experts, top-8, hidden 6144, intermediate 2048), the
+skewed decode layer (512 tokens, Zipf-biased router) and the prefill layer (16384
+tokens), in the launch configuration the benchmark times.  Where the oracle cannot
+finish the whole prefill layer in seconds, stages are checked on sampled rows with
+oracle-produced inputs.
+"""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.parity import (bf16_values, check_bf16, dev, dev_bf16, host_bits, np_bf16_round,
+                          swiglu_ref_and_bound)
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("block_scaled_fp4_02_amd")
+
+
+def log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------------------
+# weights shared by the full-size layers (same seed and expert count -> same weights)
+
+_WEIGHTS = {}
+
+
+def layer_weights(L: synth.Layer):
+    """Oracle-quantised NVFP4 weights of all experts, host and device copies (cached)."""
+    key = (L.E, L.H, L.I)
+    if key not in _WEIGHTS:
+        log(f"generating + oracle-quantising weights E={L.E} H={L.H} I={L.I}")
+        W1 = synth.per_expert(lambda e: oracle.quantize(synth.layer_w1(L, e)), range(L.E))
+        W2 = synth.per_expert(lambda e: oracle.quantize(synth.layer_w2(L, e)), range(L.E))
+        d1 = moe.NVFP4Tensor(dev(np.stack([w.q for w in W1])), dev(np.stack([w.sf for w in W1])),
+                             dev(np.array([w.g for w in W1], np.float32)))
+        d2 = moe.NVFP4Tensor(dev(np.stack([w.q for w in W2])), dev(np.stack([w.sf for w in W2])),
+                             dev(np.array([w.g for w in W2], np.float32)))
+        _WEIGHTS[key] = (W1, W2, d1, d2)
+        log("weights ready")
+    return _WEIGHTS[key]
+
+
+def stack(W):
+    return (np.stack([w.q for w in W]), np.stack([w.sf for w in W]),
+            np.array([w.g for w in W], np.float32))
+
+
+# ---------------------------------------------------------------------------------------
+# routing and permutation: bit-exact
+
+def _check_route(logits: np.ndarray, k: int):
+    T, E = logits.shape
+    log(f"route_permute T={T} E={E} k={k}")
+    ids_o, w_o = oracle.route(logits, k) if T else (np.zeros((0, k), np.int32), np.zeros((0, k)))
+    off_o, rs_o, tsr_o = oracle.permute(ids_o, E)
+    ids, w, off, rs, tsr = moe.route_permute_alloc(dev(logits) if T else torch.empty(0, E, device="cuda"), k)
+    torch.cuda.synchronize()
+    assert np.array_equal(off.cpu().numpy(), off_o)
+    if T:
+        assert np.array_equal(ids.cpu().numpy(), ids_o)
+        assert np.array_equal(rs.cpu().numpy(), rs_o)
+        assert np.array_equal(tsr.cpu().numpy(), tsr_o)
+        wg = w.cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(wg - w_o) / w_o) <= 1e-6
+
+
+@pytest.mark.parametrize("L", [synth.TINY, synth.LAYER_DECODE, synth.LAYER_SKEWED, synth.LAYER_PREFILL],
+                         ids=lambda L: L.name)
+def test_route_permute_workloads(L):
+    _check_route(synth.router_logits(L), L.k)
+
+
+@pytest.mark.parametrize("T,E,k", [(0, 8, 2), (1, 1, 1), (37, 1024, 32), (100, 8, 8), (300, 3, 2), (257, 256, 8)])
+def test_route_permute_edges(T, E, k):
+    rng = np.random.default_rng(T * 7 + E + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    _check_route(logits, k)
+
+
+def test_route_permute_ties_and_infinities():
+    rng = np.random.default_rng(3)
+    logits = rng.integers(-2, 3, (513, 64)).astype(np.float32)  # heavy ties
+    logits[5, :] = 0.0
+    logits[6, 10] = -0.0
+    logits[7, :] = -np.inf
+    logits[7, 3] = 1.0
+    _check_route(logits, 8)
+
+
+# ---------------------------------------------------------------------------------------
+# quantisation: bit-exact
+
+def _check_quant(x32: np.ndarray, bf16: bool, g=None, partials=None):
+    rows, cols = x32.shape
+    log(f"quantize rows={rows} C={cols} bf16={bf16} static={g is not None} partials={partials is not None}")
+    ref = oracle.quantize(x32, g)
+    xt = dev_bf16(synth.bf16_bits(x32)) if bf16 else dev(x32)
+    gs = dev(np.array([g], np.float32)) if g is not None else None
+    amax_in = dev(partials) if partials is not None else None
+    t = moe.quantize_alloc(xt, gs=gs, amax_in=amax_in)
+    torch.cuda.synchronize()
+    assert np.array_equal(t.q.cpu().numpy(), ref.q)
+    assert np.array_equal(t.sf.cpu().numpy(), ref.sf)
+    assert t.gs.cpu().numpy().view(np.uint32)[0] == np.float32(ref.g).view(np.uint32)
+
+
+def test_quantize_activations_bf16():
+    L = synth.LAYER_DECODE
+    x = synth.bf16_to_f32(synth.layer_activations(L))
+    _check_quant(x, bf16=True)
+
+
+def test_quantize_weights_f32():
+    L = synth.LAYER_DECODE
+    _check_quant(synth.layer_w1(L, 3), bf16=False)
+
+
+def test_quantize_static_and_partials():
+    rng = np.random.default_rng(1)
+    x = synth.bf16_to_f32(synth.bf16_bits(rng.standard_normal((300, 2048)).astype(np.float32) * 3))
+    _check_quant(x, bf16=True, g=0.0123)
+    parts = np.zeros(997, np.float32)
+    parts[17] = np.abs(x).max()
+    parts[3] = np.abs(x).max() / 2
+    _check_quant(x, bf16=True, partials=parts)
+
+
+@pytest.mark.parametrize("case", ["zeros", "tiny_block", "wide_range", "one_block", "negzero"])
+def test_quantize_edges(case):
+    rng = np.random.default_rng(5)
+    if case == "zeros":
+        x = np.zeros((4, 64), np.float32)
+    elif case == "tiny_block":
+        x = rng.standard_normal((8, 64)).astype(np.float32)
+        x[3, 16:32] *= 1e-7
+    elif case == "wide_range":
+        x = (rng.standard_normal((64, 256)) * np.exp(rng.uniform(-20, 20, (64, 1)))).astype(np.float32)
+    elif case == "one_block":
+        x = rng.standard_normal((1, 16)).astype(np.float32)
+    else:
+        x = -np.zeros((3, 32), np.float32)
+        x[1, 5] = 2.0
+    _check_quant(x, bf16=False)
+
+
+# ---------------------------------------------------------------------------------------
+# grouped GEMM, NONE epilogue
+
+def _gemm_case(sizes, K, N, gather, seed):
+    rng = np.random.default_rng(seed)
+    E = len(sizes)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(off[-1])
+    T = max(R, 1) + 5
+    A = oracle.quantize_bf16(synth.bf16_bits(rng.standard_normal((T, K)).astype(np.float32)))
+    Bs = [oracle.quantize((rng.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in range(E)]
+    A_rows = rng.integers(0, T, R).astype(np.int32) if gather else None
+    return A, Bs, off, A_rows, R
+
+
+def _run_gemm_none(A, Bs, off, A_rows, R, label):
+    log(f"gemm NONE {label}: E={len(Bs)} R={R} N={Bs[0].q.shape[0]} K={A.q.shape[1] * 2}")
+    Bq, Bsf, gB = stack(Bs)
+    ref = oracle.grouped_gemm(A, Bq, Bsf, gB, off, A_rows=A_rows)
+    dA = moe.NVFP4Tensor(dev(A.q), dev(A.sf), dev(np.array([A.g], np.float32)))
+    dB = moe.NVFP4Tensor(dev(Bq), dev(Bsf), dev(gB))
+    D = moe.grouped_gemm_alloc(dA, dB, dev(off), R, moe.MOE_EPI_NONE,
+                               A_rows=dev(A_rows) if A_rows is not None else None)
+    torch.cuda.synchronize()
+    got = host_bits(D)
+    if R:
+        check_bf16(got, ref, f"gemm NONE {label}")
+        exact = (got == np_bf16_round(ref)).mean()
+        print(f"  bf16-exact fraction {exact:.5f}", flush=True)
+        assert exact > 0.98
+
+
+@pytest.mark.parametrize("sizes,K,N,gather", [
+    ([8, 6, 9, 9], 256, 512, True),                       # tiny layer shape, gate/up as one GEMM
+    ([0, 1, 31, 32, 33, 64, 65, 130, 0], 512, 256, True),  # ragged groups, empty groups, tails
+    ([40, 0, 3], 1536, 256, False),                       # K split 2 ways inside a workgroup
+    ([7, 25], 1024, 512, False),                          # K split 4 ways
+    ([0, 0, 0], 256, 256, False),                         # no rows at all
+    ([300], 256, 768, True),                              # one big group: several row chunks
+])
+def test_gemm_none_shapes(sizes, K, N, gather):
+    A, Bs, off, A_rows, R = _gemm_case(sizes, K, N, gather, seed=sum(sizes) + K + N)
+    _run_gemm_none(A, Bs, off, A_rows, R, f"sizes={sizes}")
+
+
+def test_gemm_none_decode_grouped_gemm_full():
+    """8 groups x 32 rows, K 6144, N 2048, NONE epilogue -- the single grouped GEMM."""
+    G = synth.GEMM_DECODE
+    A = oracle.quantize_bf16(synth.gemm_a_bf16(G))
+    Bs = synth.per_expert(lambda e: oracle.quantize(synth.gemm_b(G, e)), range(G.E))
+    off = np.arange(0, (G.E + 1) * G.M, G.M, dtype=np.int32)
+    _run_gemm_none(A, Bs, off, None, G.E * G.M, "decode 8x32x6144x2048")
+
+
+# ---------------------------------------------------------------------------------------
+# grouped GEMM, SwiGLU epilogue, and the requantisation that consumes it
+
+def _run_gemm_swiglu(A, Bs, off, A_rows, R, label, rows=None):
+    log(f"gemm SWIGLU {label}: E={len(Bs)} R={R}")
+    Bq, Bsf, gB = stack(Bs)
+    dA = moe.NVFP4Tensor(dev(A.q), dev(A.sf), dev(np.array([A.g], np.float32)))
+    dB = moe.NVFP4Tensor(dev(Bq), dev(Bsf), dev(gB))
+    act, amax = moe.grouped_gemm_alloc(dA, dB, dev(off), R, moe.MOE_EPI_SWIGLU,
+                                       A_rows=dev(A_rows) if A_rows is not None else None)
+    torch.cuda.synchronize()
+    got_all = host_bits(act)
+    # partial maxima: their maximum is max |act| (a property of the kernel's own output)
+    assert amax.max().item() == np.abs(bf16_values(got_all)).max(initial=0.0)
+    rows = np.arange(R, dtype=np.int32) if rows is None else rows
+    y1 = oracle.grouped_gemm(A, Bq, Bsf, gB, off, A_rows=A_rows, rows=rows)
+    ref, bound = swiglu_ref_and_bound(y1, np_bf16_round)
+    got = bf16_values(got_all[rows])
+    diff = np.abs(got - ref)
+    print(f"  act: max diff {diff.max():.3e}, max bound-ratio {(diff / bound).max():.3f}, "
+          f"exact {(got_all[rows] == oracle.swiglu(y1)).mean():.5f}", flush=True)
+    assert (diff <= bound).all()
+    check_bf16(got_all[rows], ref, f"gemm SWIGLU {label} (north-star bar)")
+
+
+@pytest.mark.parametrize("sizes,K,I", [([8, 6, 9, 9], 256, 256), ([0, 17, 33, 64, 65, 1], 512, 384)])
+def test_gemm_swiglu_shapes(sizes, K, I):
+    A, Bs, off, A_rows, R = _gemm_case(sizes, K, 2 * I, True, seed=7 + K + I)
+    _run_gemm_swiglu(A, Bs, off, A_rows, R, f"sizes={sizes}")
+
+
+def test_requantize_bit_exact_from_partials():
+    rng = np.random.default_rng(9)
+    act = synth.bf16_bits((rng.standard_normal((8192, 2048)) * 2).astype(np.float32))
+    x = synth.bf16_to_f32(act)
+    parts = np.zeros(4096, np.float32)
+    parts[rng.integers(0, 4096, 50)] = np.abs(x).max() * rng.uniform(0, 1, 50).astype(np.float32)
+    parts[1234] = np.abs(x).max()
+    _check_quant(x, bf16=True, partials=parts)
+
+
+# ---------------------------------------------------------------------------------------
+# FINALIZE
+
+@pytest.mark.parametrize("T,E,k,H", [(16, 4, 2, 256), (1024, 256, 8, 6144), (5, 3, 3, 8), (64, 32, 1, 512)])
+def test_finalize(T, E, k, H):
+    log(f"finalize T={T} k={k} H={H}")
+    rng = np.random.default_rng(T + H)
+    ids, w = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    off, rs, tsr = oracle.permute(ids, E)
+    w32 = w.astype(np.float32)
+    Y = synth.bf16_bits((rng.standard_normal((T * k, H)) * 3).astype(np.float32))
+    ref64, _ = oracle.finalize(bf16_values(Y), w32.astype(np.float64), tsr)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    moe.moe_finalize(dev_bf16(Y), dev(w32), dev(tsr), out)
+    torch.cuda.synchronize()
+    got = host_bits(out)
+    check_bf16(got, ref64, f"finalize T={T} k={k} H={H}")
+    assert (got == np_bf16_round(ref64)).mean() > 0.99
+
+
+# ---------------------------------------------------------------------------------------
+# the whole layer, end to end
+
+def _layer_gpu(L, logits, x_bits, d1, d2):
+    plan = moe.MoELayerPlan(L.T, L.E, L.k, L.H, L.I, d1, d2)
+    out = plan.forward(dev(logits), dev_bf16(x_bits))
+    torch.cuda.synchronize()
+    return plan, host_bits(out)
+
+
+def test_layer_tiny_end_to_end():
+    L = synth.TINY
+    logits, x = synth.router_logits(L), synth.layer_activations(L)
+    W1 = [oracle.quantize(synth.layer_w1(L, e)) for e in range(L.E)]
+    W2 = [oracle.quantize(synth.layer_w2(L, e)) for e in range(L.E)]
+    r = oracle.moe_layer(logits, x, W1, W2, L.k)
+    q1, q2 = stack(W1), stack(W2)
+    d1 = moe.NVFP4Tensor(*(dev(a) for a in q1))
+    d2 = moe.NVFP4Tensor(*(dev(a) for a in q2))
+    plan, got = _layer_gpu(L, logits, x, d1, d2)
+    assert np.array_equal(plan.off.cpu().numpy(), r.offsets)
+    assert np.array_equal(plan.xq.q.cpu().numpy(), r.xq.q)
+    check_bf16(got, r.out64, "layer tiny")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("L", [synth.LAYER_DECODE, synth.LAYER_SKEWED], ids=lambda L: L.name)
+def test_layer_full_size_end_to_end(L):
+    W1, W2, d1, d2 = layer_weights(L)
+    logits, x = synth.router_logits(L), synth.layer_activations(L)
+    log(f"layer {L.name}: GPU forward")
+    plan, got = _layer_gpu(L, logits, x, d1, d2)
+    log(f"layer {L.name}: oracle")
+    r = oracle.moe_layer(logits, x, W1, W2, L.k)
+    log(f"layer {L.name}: compare")
+    sizes = np.diff(r.offsets)
+    print(f"  rows per expert: min {sizes.min()} median {int(np.median(sizes))} max {sizes.max()} "
+          f"empty {(sizes == 0).sum()}", flush=True)
+    assert np.array_equal(plan.off.cpu().numpy(), r.offsets)
+    assert np.array_equal(plan.row_src.cpu().numpy(), r.row_src)
+    assert np.array_equal(plan.xq.q.cpu().numpy(), r.xq.q) and np.array_equal(plan.xq.sf.cpu().numpy(), r.xq.sf)
+    check_bf16(got, r.out64, f"layer {L.name} out")
+
+
+@pytest.mark.timeout(600)
+def test_layer_prefill_stages_sampled():
+    """Prefill layer (16384 tokens, ~512 rows per expert) in the benchmark's launch
+    configuration; each stage is checked against the oracle on oracle-produced inputs,
+    on sampled rows where the whole stage is too slow for the oracle."""
+    L = synth.LAYER_PREFILL
+    W1, W2, d1, d2 = layer_weights(L)
+    logits, x = synth.router_logits(L), synth.layer_activations(L)
+    ids_o, w_o = oracle.route(logits, L.k)
+    off_o, rs_o, tsr_o = oracle.permute(ids_o, L.E)
+    xq_o = oracle.quantize_bf16(x)
+    log("prefill: GPU forward")
+    plan, got_out = _layer_gpu(L, logits, x, d1, d2)
+    assert np.array_equal(plan.ids.cpu().numpy(), ids_o)
+    assert np.array_equal(plan.off.cpu().numpy(), off_o)
+    assert np.array_equal(plan.tsr.cpu().numpy(), tsr_o)
+    assert np.array_equal(plan.xq.q.cpu().numpy(), xq_o.q)
+    assert np.isfinite(bf16_values(got_out)).all()
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(L.R, 96, replace=False)).astype(np.int32)
+    # GEMM1 + SwiGLU on sampled rows (inputs identical: the quantised x matched bit for bit)
+    log("prefill: GEMM1 sampled rows")
+    B1 = stack(W1)
+    y1 = oracle.grouped_gemm(xq_o, *B1, off_o, A_rows=rs_o, rows=sample)
+    ref, bound = swiglu_ref_and_bound(y1, np_bf16_round)
+    got = bf16_values(host_bits(plan.act)[sample])
+    assert (np.abs(got - ref) <= bound).all()
+    # GEMM2 on an oracle-quantised intermediate, sampled rows, in the same launch config
+    log("prefill: GEMM2 sampled rows on oracle-quantised input")
+    act_o = synth.bf16_bits((rng.standard_normal((L.R, L.I)) * 1.5).astype(np.float32))
+    aq = oracle.quantize_bf16(act_o)
+    plan.actq.q.copy_(dev(aq.q)); plan.actq.sf.copy_(dev(aq.sf)); plan.actq.gs.copy_(dev(np.array([aq.g], np.float32)))
+    plan.gemm2()
+    torch.cuda.synchronize()
+    B2 = stack(W2)
+    y2s = oracle.grouped_gemm(aq, *B2, off_o, rows=sample)
+    check_bf16(host_bits(plan.Y)[sample], y2s, "prefill GEMM2 sampled rows")
+
+
+# ---------------------------------------------------------------------------------------
+# determinism: identical bytes on a repeated run (no float atomics anywhere)
+
+def test_layer_deterministic():
+    L = synth.Layer("mid_t256_e32_k4_h512_i256", T=256, E=32, k=4, H=512, I=256)
+    rng = np.random.default_rng(2)
+    W1 = [oracle.quantize((rng.standard_normal((2 * L.I, L.H)) * 0.02).astype(np.float32)) for _ in range(L.E)]
+    W2 = [oracle.quantize((rng.standard_normal((L.H, L.I)) * 0.02).astype(np.float32)) for _ in range(L.E)]
+    d1 = moe.NVFP4Tensor(*(dev(a) for a in stack(W1)))
+    d2 = moe.NVFP4Tensor(*(dev(a) for a in stack(W2)))
+    logits = rng.standard_normal((L.T, L.E)).astype(np.float32)
+    x = synth.bf16_bits(rng.standard_normal((L.T, L.H)).astype(np.float32))
+    plan = moe.MoELayerPlan(L.T, L.E, L.k, L.H, L.I, d1, d2)
+    outs = []
+    for _ in range(3):
+        o = plan.forward(dev(logits), dev_bf16(x))
+        torch.cuda.synchronize()
+        outs.append((host_bits(o).copy(), host_bits(plan.act).copy(), plan.actq.q.cpu().numpy().copy()))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
+    r = oracle.moe_layer(logits, x, W1, W2, L.k)
+    check_bf16(outs[0][0], r.out64, "layer mid (E=32)")
