@@ -42,7 +42,8 @@ def parse():
 
 def make_weights(L, moe, torch):
     """Seeded f32 weights per expert (host threads), uploaded and NVFP4-quantised on the GPU
-    by the library's own quantiser, one dynamic global scale per expert matrix."""
+    by the library's own quantiser, one dynamic global scale per expert matrix, then packed
+    once into the layout the grouped GEMM streams (moe_pack_weights_nvfp4)."""
     import synth
     from concurrent.futures import ThreadPoolExecutor
     dev = torch.device("cuda")
@@ -63,7 +64,10 @@ def make_weights(L, moe, torch):
                 staging.copy_(torch.from_numpy(w))
                 moe.moe_quantize_nvfp4(staging, q[e], sf[e], gs[e:e + 1], moe.MOE_GS_DYNAMIC, None, ws)
         torch.cuda.synchronize()
-        out[name] = moe.NVFP4Tensor(q, sf, gs)
+        packed = moe.pack_weights(moe.NVFP4Tensor(q, sf, gs))   # one-time layout preparation
+        torch.cuda.synchronize()
+        del q, sf, staging
+        out[name] = packed
     return out["W1"], out["W2"]
 
 
@@ -175,7 +179,8 @@ def main():
         "config": {"workload": L.name, "tokens": L.T, "experts": L.E, "top_k": L.k, "hidden": L.H,
                    "intermediate": L.I, "rows_per_expert_min_median_max": [int(sizes.min()), int(np.median(sizes)),
                                                                            int(sizes.max())],
-                   "operands": "NVFP4 (e2m1, e4m3 scale per 16, f32 global) dequantised exactly to fp16 MFMA, fp32 accumulate"},
+                   "operands": "NVFP4 (e2m1, e4m3 scale per 16, f32 global) dequantised exactly to fp16 MFMA, fp32 accumulate",
+                   "weights_layout": "packed"},
         "roofline": {"kernel": "grouped_gemm_kernel (gate/up + SwiGLU)", "bound": "hbm",
                      "achieved": round(g1_alg_bytes / g1_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(g1_alg_bytes / g1_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,

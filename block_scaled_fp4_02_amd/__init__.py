@@ -25,6 +25,7 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE
 MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
 MOE_GS_STATIC, MOE_GS_DYNAMIC = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
+MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_PACKED = 0, 1
 
 EXPORTED = [
     "moe_status_string", "moe_last_hip_error",
@@ -32,6 +33,7 @@ EXPORTED = [
     "moe_quantize_nvfp4_workspace", "moe_quantize_nvfp4",
     "moe_grouped_gemm_nvfp4_workspace", "moe_grouped_gemm_nvfp4_amax_slots",
     "moe_grouped_gemm_nvfp4_can_implement", "moe_grouped_gemm_nvfp4",
+    "moe_pack_weights_nvfp4_bytes", "moe_pack_weights_nvfp4",
     "moe_finalize",
 ]
 
@@ -52,6 +54,7 @@ class moe_gemm_args(C.Structure):
         ("R", C.c_int64),
         ("epilogue", C.c_int32),
         ("D", C.c_void_p), ("amax_out", C.c_void_p),
+        ("B_layout", C.c_int32),
     ]
 
 
@@ -79,6 +82,8 @@ def lib():
             "moe_grouped_gemm_nvfp4_amax_slots": (i64, [args_p]),
             "moe_grouped_gemm_nvfp4_can_implement": (i32, [args_p]),
             "moe_grouped_gemm_nvfp4": (i32, [args_p, P, sz, P]),
+            "moe_pack_weights_nvfp4_bytes": (sz, [i64, i32]),
+            "moe_pack_weights_nvfp4": (i32, [P, P, i64, i32, P, P]),
             "moe_finalize": (i32, [P, i64, P, P, i32, i32, i32, P, P]),
         }
         for name, (res, argt) in sig.items():
@@ -130,14 +135,23 @@ def moe_quantize_nvfp4(x, q, sf, gs, gs_mode=MOE_GS_DYNAMIC, amax_in=None, ws=No
 
 
 def make_gemm_args(A, A_sf, A_gs, B, B_sf, B_gs, expert_offsets, R, epilogue, D=None,
-                   amax_out=None, A_rows=None) -> moe_gemm_args:
-    E, N, half_k = B.shape
+                   amax_out=None, A_rows=None, N=None, K=None) -> moe_gemm_args:
+    """B / B_sf are row-major NVFP4 [E, N, K/2] / [E, N, K/16]; pass B_sf=None and B as the
+    packed buffer [E, N*K*9/16 bytes] (moe_pack_weights_nvfp4) with N and K for the packed
+    layout."""
+    packed = B_sf is None
+    if packed:
+        E = B.shape[0]
+    else:
+        E, N, half_k = B.shape
+        K = 2 * half_k
     a = moe_gemm_args()
     a.A, a.A_sf, a.A_gs, a.A_rows = _p(A), _p(A_sf), _p(A_gs), _p(A_rows)
     a.rows_A = A.shape[0]
     a.B, a.B_sf, a.B_gs, a.expert_offsets = _p(B), _p(B_sf), _p(B_gs), _p(expert_offsets)
-    a.E, a.N, a.K, a.R, a.epilogue = E, N, 2 * half_k, int(R), epilogue
+    a.E, a.N, a.K, a.R, a.epilogue = E, N, K, int(R), epilogue
     a.D, a.amax_out = _p(D), _p(amax_out)
+    a.B_layout = MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_ROWMAJOR
     return a
 
 
@@ -158,6 +172,14 @@ def moe_grouped_gemm_nvfp4(args: moe_gemm_args, ws, stream=None):
            lib().moe_grouped_gemm_nvfp4(C.byref(args), _p(ws), ws.numel(), _stream(stream)))
 
 
+def moe_pack_weights_nvfp4(B, B_sf, packed, stream=None):
+    """B [..., K/2] codes and B_sf [..., K/16] scales of rows*K elements -> packed bytes."""
+    K = B.shape[-1] * 2
+    rows = B.numel() // (K // 2)
+    _check("moe_pack_weights_nvfp4", lib().moe_pack_weights_nvfp4(
+        _p(B), _p(B_sf), rows, K, _p(packed), _stream(stream)))
+
+
 def moe_finalize(Y, topk_w, token_slot_row, out, stream=None):
     T, k = topk_w.shape
     H = out.shape[1]
@@ -173,6 +195,26 @@ class NVFP4Tensor:
     q: torch.Tensor
     sf: torch.Tensor
     gs: torch.Tensor
+
+
+@dataclass
+class PackedWeights:
+    """Expert weights [E, N, K] in the packed layout: data [E, N*K*9/16] u8, gs [E] f32."""
+    data: torch.Tensor
+    gs: torch.Tensor
+    N: int
+    K: int
+
+
+def pack_weights(W: NVFP4Tensor, stream=None) -> PackedWeights:
+    E, N, half_k = W.q.shape
+    K = 2 * half_k
+    nbytes = lib().moe_pack_weights_nvfp4_bytes(E * N, K)
+    if nbytes == 0:
+        raise MoeError("moe_pack_weights_nvfp4_bytes", MOE_ERR_UNSUPPORTED, "rows % 32 or K % 256")
+    data = torch.empty(E, nbytes // E, dtype=torch.uint8, device=W.q.device)
+    moe_pack_weights_nvfp4(W.q, W.sf, data, stream)
+    return PackedWeights(data, W.gs, N, K)
 
 
 def quantize_alloc(x: torch.Tensor, gs=None, amax_in=None, stream=None) -> NVFP4Tensor:
@@ -198,14 +240,22 @@ def route_permute_alloc(logits: torch.Tensor, k: int, stream=None):
     return ids, w, off, row_src, tsr
 
 
-def grouped_gemm_alloc(A: NVFP4Tensor, B: NVFP4Tensor, expert_offsets, R, epilogue=MOE_EPI_NONE,
+def _gemm_args_for(A: NVFP4Tensor, B, expert_offsets, R, epilogue, D, A_rows):
+    if isinstance(B, PackedWeights):
+        return make_gemm_args(A.q, A.sf, A.gs, B.data, None, B.gs, expert_offsets, R, epilogue, D,
+                              None, A_rows, N=B.N, K=B.K)
+    return make_gemm_args(A.q, A.sf, A.gs, B.q, B.sf, B.gs, expert_offsets, R, epilogue, D, None, A_rows)
+
+
+def grouped_gemm_alloc(A: NVFP4Tensor, B, expert_offsets, R, epilogue=MOE_EPI_NONE,
                        A_rows=None, stream=None):
-    """Returns D (and the partial-maxima tensor for SWIGLU)."""
-    E, N, _ = B.q.shape
-    dev = B.q.device
+    """B: NVFP4Tensor (row-major) or PackedWeights.  Returns D (and the partial-maxima tensor
+    for SWIGLU)."""
+    N = B.N if isinstance(B, PackedWeights) else B.q.shape[1]
+    dev = A.q.device
     cols = N if epilogue == MOE_EPI_NONE else N // 2
     D = torch.empty(int(R), cols, dtype=torch.bfloat16, device=dev)
-    a = make_gemm_args(A.q, A.sf, A.gs, B.q, B.sf, B.gs, expert_offsets, R, epilogue, D, None, A_rows)
+    a = _gemm_args_for(A, B, expert_offsets, R, epilogue, D, A_rows)
     amax = None
     if epilogue == MOE_EPI_SWIGLU:
         amax = torch.empty(max(moe_grouped_gemm_nvfp4_amax_slots(a), 1), dtype=torch.float32, device=dev)
@@ -220,8 +270,8 @@ class MoELayerPlan:
     """Pre-allocated buffers and argument blocks for repeated forward passes of one layer
     shape (what a serving loop or a benchmark reuses): no allocation per call."""
 
-    def __init__(self, T: int, E: int, k: int, H: int, I: int, W1: NVFP4Tensor, W2: NVFP4Tensor,
-                 device="cuda"):
+    def __init__(self, T: int, E: int, k: int, H: int, I: int, W1, W2, device="cuda"):
+        """W1 / W2: NVFP4Tensor (row-major) or PackedWeights (the fast decode layout)."""
         self.T, self.E, self.k, self.H, self.I = T, E, k, H, I
         R = T * k
         self.R = R
@@ -235,12 +285,10 @@ class MoELayerPlan:
         self.Y = z(R, H, dt=torch.bfloat16)
         self.out = z(T, H, dt=torch.bfloat16)
         self.W1, self.W2 = W1, W2
-        self.args1 = make_gemm_args(self.xq.q, self.xq.sf, self.xq.gs, W1.q, W1.sf, W1.gs, self.off, R,
-                                    MOE_EPI_SWIGLU, self.act, None, self.row_src)
+        self.args1 = _gemm_args_for(self.xq, W1, self.off, R, MOE_EPI_SWIGLU, self.act, self.row_src)
         self.amax = z(max(moe_grouped_gemm_nvfp4_amax_slots(self.args1), 1), dt=torch.float32)
         self.args1.amax_out = _p(self.amax)
-        self.args2 = make_gemm_args(self.actq.q, self.actq.sf, self.actq.gs, W2.q, W2.sf, W2.gs, self.off,
-                                    R, MOE_EPI_NONE, self.Y)
+        self.args2 = _gemm_args_for(self.actq, W2, self.off, R, MOE_EPI_NONE, self.Y, None)
         for a in (self.args1, self.args2):
             _check("moe_grouped_gemm_nvfp4_can_implement", moe_grouped_gemm_nvfp4_can_implement(a))
         L = lib()

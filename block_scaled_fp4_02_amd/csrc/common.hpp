@@ -56,6 +56,7 @@ hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t C, 
 size_t quantize_ws_bytes(int64_t rows, int64_t C);
 
 struct GemmPlan {
+  int chunk_rows;    // rows per work item
   int ks;            // K split across the waves of a workgroup: 1, 2 or 4
   int n_tile;        // weight rows (output columns of y) per workgroup
   int n_tiles;       // N / n_tile
@@ -66,6 +67,10 @@ struct GemmPlan {
 GemmPlan plan_gemm(const moe_gemm_args &a);
 hipError_t launch_grouped_gemm(const moe_gemm_args &a, const GemmPlan &plan, void *ws,
                                hipStream_t stream);
+
+size_t packed_weights_bytes(int64_t rows, int K);
+hipError_t launch_pack_weights(const uint8_t *B, const uint8_t *B_sf, int64_t rows, int K,
+                               uint8_t *packed, hipStream_t stream);
 
 hipError_t launch_finalize(const uint16_t *Y, int64_t R, const float *topk_w,
                            const int32_t *token_slot_row, int T, int k, int H, uint16_t *out,

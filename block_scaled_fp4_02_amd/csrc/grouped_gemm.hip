@@ -41,7 +41,9 @@ namespace moe {
 namespace {
 
 constexpr int kKStep = 256;   // K elements per wave iteration
-constexpr int kChunkRows = 64;  // rows per work item (two 32-row MFMA tiles)
+constexpr int kChunkRows = 64;    // rows per work item, row-major kernel (two 32-row MFMA tiles)
+constexpr int kChunkRows16 = 48;  // rows per work item, packed kernel (three 16-row MFMA tiles)
+constexpr int kTok16 = kChunkRows16 / 16;
 
 struct GemmParams {
   const uint8_t *A;
@@ -62,7 +64,7 @@ struct GemmParams {
 // ---- work list ---------------------------------------------------------------
 
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restrict__ offsets, int E,
-                                                        int64_t R, int n_tiles, int64_t max_items,
+                                                        int64_t R, int chunk_rows, int n_tiles, int64_t max_items,
                                                         int4 *__restrict__ items,
                                                         int *__restrict__ count) {
   __shared__ int64_t scan[1024];
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
       hi = hi < lo ? lo : (hi > R ? R : hi);
       rows = hi - lo;
     }
-    const int64_t chunks = (rows + kChunkRows - 1) / kChunkRows;
+    const int64_t chunks = (rows + chunk_rows - 1) / chunk_rows;
     const int64_t mine = chunks * n_tiles;
     scan[threadIdx.x] = mine;
     __syncthreads();
@@ -92,9 +94,9 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
       for (int64_t c = 0; c < chunks; c++) {
         const int64_t w = first + nt * chunks + c;
         if (w < max_items) {
-          const int64_t r0 = lo + c * kChunkRows;
-          const int64_t nr = rows - c * kChunkRows;
-          items[w] = make_int4(e, static_cast<int>(r0), static_cast<int>(nr < kChunkRows ? nr : kChunkRows),
+          const int64_t r0 = lo + c * chunk_rows;
+          const int64_t nr = rows - c * chunk_rows;
+          items[w] = make_int4(e, static_cast<int>(r0), static_cast<int>(nr < chunk_rows ? nr : chunk_rows),
                                static_cast<int>(nt));
         }
       }
@@ -132,10 +134,11 @@ struct Frag {       // one lane's share of a 32-row operand tile for one 256-wid
   uint2 s;          // the 8 scale bytes of blocks [8h, 8h + 8) of the step
 };
 
-// codes / scales point at the lane's row, already offset by the lane half.
-__device__ __forceinline__ void load_frag(Frag &f, const uint8_t *codes, const uint8_t *scales) {
+// codes / scales point at the lane's data for the step; qs = distance between the four
+// 16-byte code pieces (16 in the row-major layout, 1024 in the packed layout).
+__device__ __forceinline__ void load_frag(Frag &f, const uint8_t *codes, const uint8_t *scales, int qs) {
 #pragma unroll
-  for (int q = 0; q < 4; q++) f.q[q] = *reinterpret_cast<const uint4 *>(codes + 16 * q);
+  for (int q = 0; q < 4; q++) f.q[q] = *reinterpret_cast<const uint4 *>(codes + qs * q);
   f.s = *reinterpret_cast<const uint2 *>(scales);
 }
 
@@ -143,17 +146,266 @@ __device__ __forceinline__ uint32_t word(const uint4 &v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// ---- the kernel ----------------------------------------------------------------
+// ---- the packed weight layout ---------------------------------------------------
+//
+// Weights [rows, K] (rows = E * N, rows % 16 == 0, K % 256 == 0) are regrouped into
+// blocks of 2304 bytes, one per (16-row tile T, 256-wide K step s), at byte offset
+// (T * K/256 + s) * 2304, holding exactly what one wave loads for that tile and step, in
+// lane order (lane l = 16g + r, g = 0..3, r = 0..15): two 1 KB pieces q = 0..1 where lane l
+// has the 16 code bytes [32g + 16q, +16) of the step for row 16T + r, then 256 bytes where
+// lane l has the 4 scale bytes [4g, 4g + 4) of the step for row 16T + r.  Every weight load
+// of the packed kernel is one contiguous 1 KB (or 256 B) wave access with the scales in the
+// same stream.
+
+constexpr int kPackBlock = 2304;
+
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ B,
+                                                   const uint8_t *__restrict__ B_sf, int64_t rows,
+                                                   int K, uint8_t *__restrict__ out) {
+  const int steps = K / kKStep;
+  const int64_t nblocks = rows / 16 * steps;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  // per block: 128 code pieces of 16 bytes, then 64 scale pieces of 4 bytes
+  const int64_t blk = i / 192;
+  const int piece = static_cast<int>(i % 192);
+  if (blk >= nblocks) return;
+  const int64_t T = blk / steps;
+  const int s = static_cast<int>(blk % steps);
+  uint8_t *dst = out + blk * kPackBlock;
+  if (piece < 128) {
+    const int q = piece >> 6, l = piece & 63, r = l & 15, g = l >> 4;
+    const uint8_t *src = B + (T * 16 + r) * (K / 2) + s * 128 + 32 * g + 16 * q;
+    *reinterpret_cast<uint4 *>(dst + q * 1024 + l * 16) = *reinterpret_cast<const uint4 *>(src);
+  } else {
+    const int l = piece - 128, r = l & 15, g = l >> 4;
+    const uint8_t *src = B_sf + (T * 16 + r) * (K / 16) + s * 16 + 4 * g;
+    *reinterpret_cast<uint32_t *>(dst + 2048 + l * 4) = *reinterpret_cast<const uint32_t *>(src);
+  }
+}
+
+// ---- packed-weight kernel: 16x16x32 fp16 MFMA ---------------------------------------
+//
+// A wave owns four 16-row weight tiles (64 rows) and all 16-row token tiles of its chunk
+// (up to four), so padding is at most 15 token rows.  Per 256-wide K step and 16-row tile
+// a lane of group g holds the 64 elements [64g, 64g + 64) of its row: MFMA j = 4q + d (q =
+// 0..1, d = 0..3) takes dword d of piece q, elements [64g + 32q + 8d, +8), whose scale is
+// byte 2q + d/2 of the lane's scale word.  Token tiles use the same K order.
+
+struct Frag16 {   // one lane's share of a 16-row tile for one 256-wide K step
+  uint4 q[2];     // code pieces: elements [64g + 32q, +32)
+  uint32_t s;     // scale bytes of blocks [4g, 4g + 4)
+};
+
+__device__ __forceinline__ void load_frag16(Frag16 &f, const uint8_t *codes, const uint8_t *scales, int qs) {
+  f.q[0] = *reinterpret_cast<const uint4 *>(codes);
+  f.q[1] = *reinterpret_cast<const uint4 *>(codes + qs);
+  f.s = *reinterpret_cast<const uint32_t *>(scales);
+}
 
 template <int KS, int EPI>
+__global__ __launch_bounds__(256, 2) void grouped_gemm16_kernel(GemmParams P) {
+  constexpr int NG = 4 / KS;
+  constexpr int SPAN = NG * 64;   // weight rows per workgroup
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int ng = wv % NG;
+  const int kq = wv / NG;
+  const int r = lane & 15;        // row within a 16-row tile
+  const int g = lane >> 4;        // K group of the lane
+
+  const int b = blockIdx.x;
+  const int count = *P.count;
+  const int per_xcd = (count + kXcds - 1) / kXcds;
+  const int jx = b / kXcds;
+  const int w = (b % kXcds) * per_xcd + jx;
+  if (jx >= per_xcd || w >= count) {
+    if (EPI == MOE_EPI_SWIGLU && threadIdx.x == 0) P.amax_out[b] = 0.f;
+    return;
+  }
+  const int4 item = P.items[w];
+  const int e = item.x, row0 = item.y, nrows = item.z, nt = item.w;
+  const int I = P.N / 2;
+  const int steps = P.K / kKStep;
+
+  // first weight row of the wave's four 16-row tiles (SwiGLU: gate, gate, up, up)
+  int nrow[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    if (EPI == MOE_EPI_SWIGLU) {
+      const int gate = nt * (SPAN / 2) + ng * 32 + (j & 1) * 16;
+      nrow[j] = (j >= 2) ? I + gate : gate;
+    } else {
+      nrow[j] = nt * SPAN + ng * 64 + j * 16;
+    }
+  }
+  // weight tiles: wave-uniform base pointers, per-lane 32-bit offsets
+  const uint8_t *bbase[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+    bbase[j] = P.B + (static_cast<int64_t>(e) * P.N + nrow[j]) / 16 * steps * kPackBlock;
+  const uint32_t b_code_off = lane * 16, b_scale_off = 2048 + lane * 4;
+  // token rows of the (up to four) 16-row tiles of the chunk: 32-bit offsets into A
+  // (rows_A * K / 2 < 2^32 is checked on the host)
+  const int nm = (nrows + 15) / 16;
+  const uint32_t half_k = P.K / 2, k16 = P.K / 16;
+  uint32_t aoff[kTok16];
+#pragma unroll
+  for (int mt = 0; mt < kTok16; mt++) {
+    const int m = mt * 16 + r;
+    int64_t p = row0 + (m < nrows ? m : 0);
+    int64_t src = P.A_rows ? static_cast<int64_t>(P.A_rows[p]) : p;
+    src = src < 0 ? 0 : (src >= P.rows_A ? P.rows_A - 1 : src);
+    aoff[mt] = static_cast<uint32_t>(src);
+  }
+
+  float4v acc[4][kTok16];
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+#pragma unroll
+    for (int mt = 0; mt < kTok16; mt++) acc[j][mt] = float4v{};
+
+  const int s_begin = kq * (steps / KS);
+  const int iters = steps / KS;
+  Frag16 fb[4], fa[kTok16], nb[4], na[kTok16];
+  auto load_b = [&](Frag16 (&f)[4], int s) {
+    const uint32_t so = static_cast<uint32_t>(s) * kPackBlock;
+#pragma unroll
+    for (int j = 0; j < 4; j++) load_frag16(f[j], bbase[j] + (so + b_code_off), bbase[j] + (so + b_scale_off), 1024);
+  };
+  auto load_a = [&](Frag16 (&f)[kTok16], int s) {
+#pragma unroll
+    for (int mt = 0; mt < kTok16; mt++)
+      if (mt < nm)
+        load_frag16(f[mt], P.A + (aoff[mt] * half_k + 32 * g + s * (kKStep / 2)),
+                    P.A_sf + (aoff[mt] * k16 + 4 * g + s * (kKStep / 16)), 16);
+  };
+  load_a(fa, s_begin);
+  load_b(fb, s_begin);
+
+  for (int it = 0; it < iters; it++) {
+    const bool more = it + 1 < iters;
+    if (more) {
+      load_a(na, s_begin + it + 1);
+      load_b(nb, s_begin + it + 1);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        const int sb = 2 * q + (d >> 1);
+        half8 af[kTok16];
+#pragma unroll
+        for (int mt = 0; mt < kTok16; mt++)
+          if (mt < nm) af[mt] = dequant8(word(fa[mt].q[q], d), e4m3_to_f16(fa[mt].s, sb));
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const half8 bf = dequant8(word(fb[j].q[q], d), e4m3_to_f16(fb[j].s, sb));
+#pragma unroll
+          for (int mt = 0; mt < kTok16; mt++)
+            if (mt < nm) acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[mt], acc[j][mt], 0, 0, 0);
+        }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) fb[j] = nb[j];
+#pragma unroll
+      for (int mt = 0; mt < kTok16; mt++)
+        if (mt < nm) fa[mt] = na[mt];
+    }
+  }
+
+  if constexpr (KS > 1) {
+    constexpr int TILE = 4 * kTok16 * 4 * 64;
+    __shared__ float red[(KS - 1) * NG * TILE];
+    float *mine = red + ((kq - 1) * NG + ng) * TILE;
+    if (kq > 0) {
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int mt = 0; mt < kTok16; mt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) mine[((j * kTok16 + mt) * 4 + i) * 64 + lane] = acc[j][mt][i];
+    }
+    __syncthreads();
+    if (kq == 0) {
+      for (int o = 1; o < KS; o++) {
+        const float *src = red + ((o - 1) * NG + ng) * TILE;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+          for (int mt = 0; mt < kTok16; mt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) acc[j][mt][i] += src[((j * kTok16 + mt) * 4 + i) * 64 + lane];
+      }
+    }
+  }
+
+  // epilogue: 16x16 D lane layout -- weight row 4g + i, token row r of the tile
+  const float gscale = (*P.A_gs) * P.B_gs[e];
+  float amax = 0.f;
+  if (kq == 0) {
+#pragma unroll
+    for (int mt = 0; mt < kTok16; mt++) {
+      const int m = mt * 16 + r;
+      if (mt < nm && m < nrows) {
+        const int64_t p = row0 + m;
+        if (EPI == MOE_EPI_NONE) {
+          uint16_t *drow = static_cast<uint16_t *>(P.D) + p * P.N;
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const uint32_t lo = f32_to_bf16(acc[j][mt][0] * gscale) |
+                                (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][1] * gscale)) << 16);
+            const uint32_t hi = f32_to_bf16(acc[j][mt][2] * gscale) |
+                                (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][3] * gscale)) << 16);
+            *reinterpret_cast<uint2 *>(drow + nrow[j] + 4 * g) = make_uint2(lo, hi);
+          }
+        } else {
+          uint16_t *drow = static_cast<uint16_t *>(P.D) + p * I;
+#pragma unroll
+          for (int jp = 0; jp < 2; jp++) {
+            uint16_t o[4];
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+              const float gate = round_bf16(acc[jp][mt][c] * gscale);
+              const float up = round_bf16(acc[2 + jp][mt][c] * gscale);
+              const float silu = gate / (1.0f + expf(-gate));
+              o[c] = f32_to_bf16(silu * up);
+              amax = fmaxf(amax, fabsf(bf16_to_f32(o[c])));
+            }
+            *reinterpret_cast<uint2 *>(drow + nrow[jp] + 4 * g) =
+                make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+          }
+        }
+      }
+    }
+  }
+  if (EPI == MOE_EPI_SWIGLU) {
+    __shared__ float wmax[4];
+    amax = wave_max(amax);
+    if (lane == 0) wmax[wv] = amax;
+    __syncthreads();
+    if (threadIdx.x == 0) P.amax_out[b] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  }
+}
+
+// ---- the kernel ----------------------------------------------------------------
+//
+// Row-major weights, 32x32x16 fp16 MFMA.  KS: K split across the waves of a workgroup
+// (1, 2, 4); NG = 4 / KS wave groups along N; each wave owns two 32-row weight tiles (with
+// the SwiGLU epilogue a (gate, up) pair), so a workgroup covers NG * 64 weight rows.
+template <int KS, int EPI>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmParams P) {
-  constexpr int NG = 4 / KS;  // groups of 64 weight rows per workgroup
+  constexpr int TPW = 2;
+  constexpr int NG = 4 / KS;
+  constexpr int SPAN = NG * TPW * 32;                  // weight rows per workgroup
+  constexpr int QS = 16;                               // code piece stride
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int ng = wv % NG;
   const int kq = wv / NG;
   const int r = lane & 31;    // row within a 32-row tile
-  const int h = lane >> 5;    // lane half: which 32 of each 64 K elements
+  const int h = lane >> 5;    // lane half: which 128 of each 256 K elements
 
   // work item for this workgroup (contiguous ranges per XCD)
   const int b = blockIdx.x;
@@ -168,25 +420,32 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmParams P) {
   const int4 item = P.items[w];
   const int e = item.x, row0 = item.y, nrows = item.z, nt = item.w;
   const int I = P.N / 2;
+  const int steps = P.K / kKStep;
 
-  // weight rows of this wave's two 32-row tiles
-  int nrow[2];
-  if (EPI == MOE_EPI_SWIGLU) {
-    nrow[0] = nt * (NG * 32) + ng * 32;  // gate
-    nrow[1] = I + nrow[0];               // matching up rows
-  } else {
-    nrow[0] = nt * (NG * 64) + ng * 64;
-    nrow[1] = nrow[0] + 32;
+  // first weight row of each of this wave's tiles
+  int nrow[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; j++) {
+    if (EPI == MOE_EPI_SWIGLU) {
+      const int gate = nt * (SPAN / 2) + (ng * (TPW / 2) + j / 2) * 32;
+      nrow[j] = (j & 1) ? I + gate : gate;
+    } else {
+      nrow[j] = nt * SPAN + (ng * TPW + j) * 32;
+    }
   }
   const int64_t half_k = P.K / 2, k16 = P.K / 16;
-  const uint8_t *bq[2];
-  const uint8_t *bs[2];
+  const uint8_t *bq[TPW];
+  const uint8_t *bs[TPW];
 #pragma unroll
-  for (int s = 0; s < 2; s++) {
-    const int64_t row = static_cast<int64_t>(e) * P.N + nrow[s] + r;
-    bq[s] = P.B + row * half_k + 64 * h;
-    bs[s] = P.B_sf + row * k16 + 8 * h;
+  for (int j = 0; j < TPW; j++) {
+    const int64_t row = static_cast<int64_t>(e) * P.N + nrow[j];
+    bq[j] = P.B + (row + r) * half_k + 64 * h;
+    bs[j] = P.B_sf + (row + r) * k16 + 8 * h;
   }
+  // per-step advance of the weight pointers
+  const int64_t b_code_step = kKStep / 2;
+  const int64_t b_scale_step = kKStep / 16;
+
   // activation rows of the (one or two) 32-row tiles of the chunk
   const int nm = nrows > 32 ? 2 : 1;
   const uint8_t *aq[2];
@@ -201,57 +460,51 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmParams P) {
     as[mt] = P.A_sf + src * k16 + 8 * h;
   }
 
-  float16v acc[2][2];
+  float16v acc[TPW][2];
 #pragma unroll
-  for (int s = 0; s < 2; s++)
+  for (int j = 0; j < TPW; j++)
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++) acc[s][mt] = float16v{};
+    for (int mt = 0; mt < 2; mt++) acc[j][mt] = float16v{};
 
-  const int k_len = P.K / KS;
-  const int k_begin = kq * k_len;
-  const int iters = k_len / kKStep;
+  const int s_begin = kq * (steps / KS);
+  const int iters = steps / KS;
 
-  Frag fb[2], fa[2], nb[2], na[2];
+  Frag fb[TPW], fa[2], nb[TPW], na[2];
 #pragma unroll
-  for (int s = 0; s < 2; s++) load_frag(fb[s], bq[s] + k_begin / 2, bs[s] + k_begin / 16);
-  load_frag(fa[0], aq[0] + k_begin / 2, as[0] + k_begin / 16);
-  if (nm == 2) load_frag(fa[1], aq[1] + k_begin / 2, as[1] + k_begin / 16);
+  for (int j = 0; j < TPW; j++) load_frag(fb[j], bq[j] + s_begin * b_code_step, bs[j] + s_begin * b_scale_step, QS);
+  load_frag(fa[0], aq[0] + s_begin * (kKStep / 2), as[0] + s_begin * (kKStep / 16), 16);
+  if (nm == 2) load_frag(fa[1], aq[1] + s_begin * (kKStep / 2), as[1] + s_begin * (kKStep / 16), 16);
 
   for (int it = 0; it < iters; it++) {
-    const int kn = k_begin + (it + 1) * kKStep;
+    const int sn = s_begin + it + 1;
     const bool more = it + 1 < iters;
     if (more) {  // prefetch the next K step while this one computes
+      load_frag(na[0], aq[0] + sn * (kKStep / 2), as[0] + sn * (kKStep / 16), 16);
+      if (nm == 2) load_frag(na[1], aq[1] + sn * (kKStep / 2), as[1] + sn * (kKStep / 16), 16);
 #pragma unroll
-      for (int s = 0; s < 2; s++) load_frag(nb[s], bq[s] + kn / 2, bs[s] + kn / 16);
-      load_frag(na[0], aq[0] + kn / 2, as[0] + kn / 16);
-      if (nm == 2) load_frag(na[1], aq[1] + kn / 2, as[1] + kn / 16);
+      for (int j = 0; j < TPW; j++) load_frag(nb[j], bq[j] + sn * b_code_step, bs[j] + sn * b_scale_step, QS);
     }
 #pragma unroll
     for (int q = 0; q < 4; q++) {
 #pragma unroll
       for (int d = 0; d < 4; d++) {
-        // dword d of load q: elements [128h + 32q + 8d, +8), scale block 8h + 2q + d/2,
+        // dword d of piece q: elements [128h + 32q + 8d, +8), scale block 8h + 2q + d/2,
         // i.e. byte 2(q % 2) + d/2 of scale word q/2
         const int sw = q >> 1, sb = 2 * (q & 1) + (d >> 1);
-        half8 bf[2];
-#pragma unroll
-        for (int s = 0; s < 2; s++)
-          bf[s] = dequant8(word(fb[s].q[q], d), e4m3_to_f16(sw ? fb[s].s.y : fb[s].s.x, sb));
         const half8 af0 = dequant8(word(fa[0].q[q], d), e4m3_to_f16(sw ? fa[0].s.y : fa[0].s.x, sb));
+        half8 af1;
+        if (nm == 2) af1 = dequant8(word(fa[1].q[q], d), e4m3_to_f16(sw ? fa[1].s.y : fa[1].s.x, sb));
 #pragma unroll
-        for (int s = 0; s < 2; s++)
-          acc[s][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[s], af0, acc[s][0], 0, 0, 0);
-        if (nm == 2) {
-          const half8 af1 = dequant8(word(fa[1].q[q], d), e4m3_to_f16(sw ? fa[1].s.y : fa[1].s.x, sb));
-#pragma unroll
-          for (int s = 0; s < 2; s++)
-            acc[s][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[s], af1, acc[s][1], 0, 0, 0);
+        for (int j = 0; j < TPW; j++) {
+          const half8 bf = dequant8(word(fb[j].q[q], d), e4m3_to_f16(sw ? fb[j].s.y : fb[j].s.x, sb));
+          acc[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af0, acc[j][0], 0, 0, 0);
+          if (nm == 2) acc[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af1, acc[j][1], 0, 0, 0);
         }
       }
     }
     if (more) {
 #pragma unroll
-      for (int s = 0; s < 2; s++) fb[s] = nb[s];
+      for (int j = 0; j < TPW; j++) fb[j] = nb[j];
       fa[0] = na[0];
       if (nm == 2) fa[1] = na[1];
     }
@@ -259,26 +512,27 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmParams P) {
 
   // K split across waves: partial tiles added in LDS in a fixed order
   if constexpr (KS > 1) {
-    __shared__ float red[(KS - 1) * NG * 2 * 2 * 16 * 64];
-    float *mine = red + ((kq - 1) * NG + ng) * (2 * 2 * 16 * 64);
+    constexpr int TILE = TPW * 2 * 16 * 64;
+    __shared__ float red[(KS - 1) * NG * TILE];
+    float *mine = red + ((kq - 1) * NG + ng) * TILE;
     if (kq > 0) {
 #pragma unroll
-      for (int s = 0; s < 2; s++)
+      for (int j = 0; j < TPW; j++)
 #pragma unroll
         for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-          for (int i = 0; i < 16; i++) mine[((s * 2 + mt) * 16 + i) * 64 + lane] = acc[s][mt][i];
+          for (int i = 0; i < 16; i++) mine[((j * 2 + mt) * 16 + i) * 64 + lane] = acc[j][mt][i];
     }
     __syncthreads();
     if (kq == 0) {
       for (int o = 1; o < KS; o++) {
-        const float *src = red + ((o - 1) * NG + ng) * (2 * 2 * 16 * 64);
+        const float *src = red + ((o - 1) * NG + ng) * TILE;
 #pragma unroll
-        for (int s = 0; s < 2; s++)
+        for (int j = 0; j < TPW; j++)
 #pragma unroll
           for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-            for (int i = 0; i < 16; i++) acc[s][mt][i] += src[((s * 2 + mt) * 16 + i) * 64 + lane];
+            for (int i = 0; i < 16; i++) acc[j][mt][i] += src[((j * 2 + mt) * 16 + i) * 64 + lane];
       }
     }
   }
@@ -295,31 +549,33 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmParams P) {
         if (EPI == MOE_EPI_NONE) {
           uint16_t *drow = static_cast<uint16_t *>(P.D) + p * P.N;
 #pragma unroll
-          for (int s = 0; s < 2; s++)
+          for (int j = 0; j < TPW; j++)
 #pragma unroll
             for (int g4 = 0; g4 < 4; g4++) {
-              uint32_t lo = f32_to_bf16(acc[s][mt][4 * g4 + 0] * gscale) |
-                            (static_cast<uint32_t>(f32_to_bf16(acc[s][mt][4 * g4 + 1] * gscale)) << 16);
-              uint32_t hi = f32_to_bf16(acc[s][mt][4 * g4 + 2] * gscale) |
-                            (static_cast<uint32_t>(f32_to_bf16(acc[s][mt][4 * g4 + 3] * gscale)) << 16);
-              *reinterpret_cast<uint2 *>(drow + nrow[s] + 8 * g4 + 4 * h) = make_uint2(lo, hi);
+              uint32_t lo = f32_to_bf16(acc[j][mt][4 * g4 + 0] * gscale) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][4 * g4 + 1] * gscale)) << 16);
+              uint32_t hi = f32_to_bf16(acc[j][mt][4 * g4 + 2] * gscale) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][4 * g4 + 3] * gscale)) << 16);
+              *reinterpret_cast<uint2 *>(drow + nrow[j] + 8 * g4 + 4 * h) = make_uint2(lo, hi);
             }
         } else {
           uint16_t *drow = static_cast<uint16_t *>(P.D) + p * I;
 #pragma unroll
-          for (int g4 = 0; g4 < 4; g4++) {
-            uint16_t o[4];
+          for (int jp = 0; jp < TPW / 2; jp++)
 #pragma unroll
-            for (int c = 0; c < 4; c++) {
-              const float gate = round_bf16(acc[0][mt][4 * g4 + c] * gscale);
-              const float up = round_bf16(acc[1][mt][4 * g4 + c] * gscale);
-              const float silu = gate / (1.0f + expf(-gate));
-              o[c] = f32_to_bf16(silu * up);
-              amax = fmaxf(amax, fabsf(bf16_to_f32(o[c])));
+            for (int g4 = 0; g4 < 4; g4++) {
+              uint16_t o[4];
+#pragma unroll
+              for (int c = 0; c < 4; c++) {
+                const float gate = round_bf16(acc[2 * jp][mt][4 * g4 + c] * gscale);
+                const float up = round_bf16(acc[2 * jp + 1][mt][4 * g4 + c] * gscale);
+                const float silu = gate / (1.0f + expf(-gate));
+                o[c] = f32_to_bf16(silu * up);
+                amax = fmaxf(amax, fabsf(bf16_to_f32(o[c])));
+              }
+              *reinterpret_cast<uint2 *>(drow + nrow[2 * jp] + 8 * g4 + 4 * h) =
+                  make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
             }
-            *reinterpret_cast<uint2 *>(drow + nrow[0] + 8 * g4 + 4 * h) =
-                make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
-          }
         }
       }
     }
@@ -333,23 +589,35 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmParams P) {
   }
 }
 
-template <int KS, int EPI>
-void launch_ks(const GemmParams &p, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<KS, EPI>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
-                     stream, p);
+template <int EPI>
+void launch_epi(const GemmParams &p, const GemmPlan &plan, bool packed, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(plan.grid)), block(256);
+  if (packed) {
+    if (plan.ks == 1) hipLaunchKernelGGL((grouped_gemm16_kernel<1, EPI>), grid, block, 0, stream, p);
+    else if (plan.ks == 2) hipLaunchKernelGGL((grouped_gemm16_kernel<2, EPI>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((grouped_gemm16_kernel<4, EPI>), grid, block, 0, stream, p);
+  } else {
+    if (plan.ks == 1) hipLaunchKernelGGL((grouped_gemm_kernel<1, EPI>), grid, block, 0, stream, p);
+    else if (plan.ks == 2) hipLaunchKernelGGL((grouped_gemm_kernel<2, EPI>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((grouped_gemm_kernel<4, EPI>), grid, block, 0, stream, p);
+  }
 }
 
 }  // namespace
 
 GemmPlan plan_gemm(const moe_gemm_args &a) {
   GemmPlan p{};
-  const int64_t chunk_bound = (a.R + kChunkRows - 1) / kChunkRows + a.E;
-  const int64_t chunk_est = std::max<int64_t>(a.E, (a.R + kChunkRows - 1) / kChunkRows);
+  const int chunk = a.B_layout == MOE_LAYOUT_PACKED ? kChunkRows16 : kChunkRows;
+  p.chunk_rows = chunk;
+  const int64_t chunk_bound = (a.R + chunk - 1) / chunk + a.E;
+  const int64_t chunk_est = std::max<int64_t>(a.E, (a.R + chunk - 1) / chunk);
+  // A workgroup covers 256 weight rows (four waves x 64); for few groups the waves split K
+  // (2 or 4 ways) so that there are at least ~2 workgroups per CU.
   p.ks = 1;
   for (int cand = 1; cand <= 4; cand *= 2) {
     if (a.K % (kKStep * cand) != 0) break;
     p.ks = cand;
-    if (chunk_est * (a.N / (256 / cand)) >= 2 * 256) break;  // at least ~2 workgroups per CU
+    if (chunk_est * (a.N / (256 / cand)) >= 2 * 256) break;
   }
   p.n_tile = 256 / p.ks;
   p.n_tiles = a.N / p.n_tile;
@@ -364,15 +632,24 @@ hipError_t launch_grouped_gemm(const moe_gemm_args &a, const GemmPlan &plan, voi
   int *count = static_cast<int *>(ws);
   int4 *items = reinterpret_cast<int4 *>(static_cast<char *>(ws) + 16);
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, stream, a.expert_offsets, a.E, a.R,
-                     plan.n_tiles, plan.max_items, items, count);
+                     plan.chunk_rows, plan.n_tiles, plan.max_items, items, count);
   GemmParams p{a.A, a.A_sf, a.A_gs, a.A_rows, a.rows_A, a.B, a.B_sf, a.B_gs, a.E, a.N, a.K,
                a.D, a.amax_out, items, count};
-  const bool swiglu = a.epilogue == MOE_EPI_SWIGLU;
-  switch (plan.ks) {
-    case 1: swiglu ? launch_ks<1, MOE_EPI_SWIGLU>(p, plan.grid, stream) : launch_ks<1, MOE_EPI_NONE>(p, plan.grid, stream); break;
-    case 2: swiglu ? launch_ks<2, MOE_EPI_SWIGLU>(p, plan.grid, stream) : launch_ks<2, MOE_EPI_NONE>(p, plan.grid, stream); break;
-    default: swiglu ? launch_ks<4, MOE_EPI_SWIGLU>(p, plan.grid, stream) : launch_ks<4, MOE_EPI_NONE>(p, plan.grid, stream); break;
-  }
+  const bool packed = a.B_layout == MOE_LAYOUT_PACKED;
+  if (a.epilogue == MOE_EPI_SWIGLU) launch_epi<MOE_EPI_SWIGLU>(p, plan, packed, stream);
+  else launch_epi<MOE_EPI_NONE>(p, plan, packed, stream);
+  return hipGetLastError();
+}
+
+size_t packed_weights_bytes(int64_t rows, int K) { return static_cast<size_t>(rows) * K / 16 * 9; }
+
+hipError_t launch_pack_weights(const uint8_t *B, const uint8_t *B_sf, int64_t rows, int K,
+                               uint8_t *packed, hipStream_t stream) {
+  const int64_t nblocks = rows / 16 * (K / kKStep);
+  const int64_t threads = nblocks * 192;
+  if (threads > 0)
+    hipLaunchKernelGGL(pack_kernel, dim3(static_cast<uint32_t>((threads + 255) / 256)), dim3(256), 0,
+                       stream, B, B_sf, rows, K, packed);
   return hipGetLastError();
 }
 

@@ -22,15 +22,19 @@ moe_status check_gemm(const moe_gemm_args *a, bool need_pointers) {
       a->rows_A < 0)
     return MOE_ERR_SHAPE;
   if (a->epilogue != MOE_EPI_NONE && a->epilogue != MOE_EPI_SWIGLU) return MOE_ERR_UNSUPPORTED;
+  if (a->B_layout != MOE_LAYOUT_ROWMAJOR && a->B_layout != MOE_LAYOUT_PACKED) return MOE_ERR_UNSUPPORTED;
   if (a->K % 16 != 0) return MOE_ERR_SHAPE;
   if (a->K % 256 != 0 || a->N % 256 != 0) return MOE_ERR_UNSUPPORTED;
   if (a->R > 0 && a->rows_A < 1) return MOE_ERR_SHAPE;
+  // the packed kernel addresses A with 32-bit byte offsets
+  if (a->B_layout == MOE_LAYOUT_PACKED && a->rows_A * (a->K / 2) >= (int64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;
   // item indices, row indices and workgroup counts stay in 32 bits
   const GemmPlan plan = plan_gemm(*a);
   if (plan.grid >= (int64_t(1) << 31) || static_cast<int64_t>(a->E) * a->N >= (int64_t(1) << 40))
     return MOE_ERR_UNSUPPORTED;
   if (need_pointers) {
-    if (!a->B || !a->B_sf || !a->B_gs || !a->expert_offsets || !a->A_gs) return MOE_ERR_NULL;
+    if (!a->B || !a->B_gs || !a->expert_offsets || !a->A_gs) return MOE_ERR_NULL;
+    if (a->B_layout == MOE_LAYOUT_ROWMAJOR && !a->B_sf) return MOE_ERR_NULL;
     if (a->R > 0 && (!a->A || !a->A_sf || !a->D)) return MOE_ERR_NULL;
     if (a->epilogue == MOE_EPI_SWIGLU && !a->amax_out) return MOE_ERR_NULL;
   }
@@ -118,6 +122,20 @@ moe_status moe_grouped_gemm_nvfp4(const moe_gemm_args *args, void *ws, size_t ws
   const GemmPlan plan = plan_gemm(*args);
   if (!ws || ws_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE;
   return launch_status(launch_grouped_gemm(*args, plan, ws, stream));
+}
+
+size_t moe_pack_weights_nvfp4_bytes(int64_t rows, int K) {
+  if (rows < 0 || K < 256 || rows % 16 != 0 || K % 256 != 0) return 0;
+  return packed_weights_bytes(rows, K);
+}
+
+moe_status moe_pack_weights_nvfp4(const uint8_t *B, const uint8_t *B_sf, int64_t rows, int K,
+                                  uint8_t *packed, hipStream_t stream) {
+  if (rows < 0 || K < 256 || rows >= (int64_t(1) << 40) / K) return MOE_ERR_SHAPE;
+  if (rows % 16 != 0 || K % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows / 16 * (K / 256) * 192 >= (int64_t(1) << 39)) return MOE_ERR_UNSUPPORTED;  // grid < 2^31
+  if (rows > 0 && (!B || !B_sf || !packed)) return MOE_ERR_NULL;
+  return launch_status(launch_pack_weights(B, B_sf, rows, K, packed, stream));
 }
 
 moe_status moe_finalize(const uint16_t *Y, int64_t R, const float *topk_w,

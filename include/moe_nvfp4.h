@@ -143,12 +143,16 @@ moe_status moe_quantize_nvfp4(const void *x, int x_dtype, int64_t rows, int64_t 
  *                   partial maxima of |D| (their maximum is max|D|; unused slots 0),
  *                   for moe_quantize_nvfp4(..., amax_in = amax_out, ...).
  * Rows p >= expert_offsets[E] of D are not written.
+ * B_layout MOE_LAYOUT_ROWMAJOR: B / B_sf as above.  MOE_LAYOUT_PACKED: B is the output of
+ * moe_pack_weights_nvfp4 for the E*N weight rows (B_sf is ignored and may be NULL); this is
+ * the layout the decode kernels stream at full HBM rate.
  * Supported: K % 256 == 0, N % 256 == 0, 1 <= E <= 65536, 0 <= R < 2^31.
  * moe_grouped_gemm_nvfp4_can_implement() returns MOE_OK exactly when the
  * launch is supported; a supported launch then cannot fail on its
  * configuration.  ws: moe_grouped_gemm_nvfp4_workspace(args) bytes.
  * ------------------------------------------------------------------------- */
 typedef enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1 } moe_epilogue;
+typedef enum moe_layout { MOE_LAYOUT_ROWMAJOR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout;
 
 typedef struct moe_gemm_args {
   const uint8_t *A;               /* [rows_A, K/2] */
@@ -165,6 +169,7 @@ typedef struct moe_gemm_args {
   int32_t epilogue;               /* moe_epilogue */
   void *D;                        /* bf16 [R, N] (NONE) or [R, N/2] (SWIGLU) */
   float *amax_out;                /* SWIGLU only */
+  int32_t B_layout;               /* moe_layout */
 } moe_gemm_args;
 
 size_t moe_grouped_gemm_nvfp4_workspace(const moe_gemm_args *args);
@@ -172,6 +177,20 @@ int64_t moe_grouped_gemm_nvfp4_amax_slots(const moe_gemm_args *args);
 moe_status moe_grouped_gemm_nvfp4_can_implement(const moe_gemm_args *args);
 moe_status moe_grouped_gemm_nvfp4(const moe_gemm_args *args, void *ws, size_t ws_bytes,
                                   hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * 3b. One-time weight preparation: regroup NVFP4 weights [rows, K] (codes B [rows, K/2],
+ * scales B_sf [rows, K/16]; rows = E*N) into the packed layout the grouped GEMM streams:
+ * per 16-row tile T and 256-wide K step s, a 2304-byte block at offset (T*K/256 + s)*2304
+ * holding, in the order the 64 lanes of a wave load them (lane 16g + r, row 16T + r), two
+ * 1 KB pieces q = 0..1 with each lane's code bytes [32g + 16q, +16) of the step, then 256
+ * bytes with each lane's scale bytes [4g, 4g + 4) of the step.  A pure byte permutation (no
+ * arithmetic): the packed buffer holds exactly rows*K*9/16 bytes.  Requires rows % 16 == 0,
+ * K % 256 == 0.
+ * ------------------------------------------------------------------------- */
+size_t moe_pack_weights_nvfp4_bytes(int64_t rows, int K);
+moe_status moe_pack_weights_nvfp4(const uint8_t *B, const uint8_t *B_sf, int64_t rows, int K,
+                                  uint8_t *packed, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * 4. FINALIZE: out[t, h] = bf16(sum_{j<k} topk_w[t, j] * Y[token_slot_row[t*k+j], h]),

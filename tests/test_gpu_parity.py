@@ -53,10 +53,9 @@ def layer_weights(L: synth.Layer):
         log(f"generating + oracle-quantising weights E={L.E} H={L.H} I={L.I}")
         W1 = synth.per_expert(lambda e: oracle.quantize(synth.layer_w1(L, e)), range(L.E))
         W2 = synth.per_expert(lambda e: oracle.quantize(synth.layer_w2(L, e)), range(L.E))
-        d1 = moe.NVFP4Tensor(dev(np.stack([w.q for w in W1])), dev(np.stack([w.sf for w in W1])),
-                             dev(np.array([w.g for w in W1], np.float32)))
-        d2 = moe.NVFP4Tensor(dev(np.stack([w.q for w in W2])), dev(np.stack([w.sf for w in W2])),
-                             dev(np.array([w.g for w in W2], np.float32)))
+        d1 = _weights(*stack(W1), packed=True)
+        d2 = _weights(*stack(W2), packed=True)
+        torch.cuda.synchronize()
         _WEIGHTS[key] = (W1, W2, d1, d2)
         log("weights ready")
     return _WEIGHTS[key]
@@ -180,12 +179,18 @@ def _gemm_case(sizes, K, N, gather, seed):
     return A, Bs, off, A_rows, R
 
 
-def _run_gemm_none(A, Bs, off, A_rows, R, label):
+def _weights(Bq, Bsf, gB, packed):
+    dB = moe.NVFP4Tensor(dev(Bq), dev(Bsf), dev(gB))
+    return moe.pack_weights(dB) if packed else dB
+
+
+def _run_gemm_none(A, Bs, off, A_rows, R, label, packed=False):
+    label = f"{label} {'packed' if packed else 'row-major'}"
     log(f"gemm NONE {label}: E={len(Bs)} R={R} N={Bs[0].q.shape[0]} K={A.q.shape[1] * 2}")
     Bq, Bsf, gB = stack(Bs)
     ref = oracle.grouped_gemm(A, Bq, Bsf, gB, off, A_rows=A_rows)
     dA = moe.NVFP4Tensor(dev(A.q), dev(A.sf), dev(np.array([A.g], np.float32)))
-    dB = moe.NVFP4Tensor(dev(Bq), dev(Bsf), dev(gB))
+    dB = _weights(Bq, Bsf, gB, packed)
     D = moe.grouped_gemm_alloc(dA, dB, dev(off), R, moe.MOE_EPI_NONE,
                                A_rows=dev(A_rows) if A_rows is not None else None)
     torch.cuda.synchronize()
@@ -197,6 +202,7 @@ def _run_gemm_none(A, Bs, off, A_rows, R, label):
         assert exact > 0.98
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
 @pytest.mark.parametrize("sizes,K,N,gather", [
     ([8, 6, 9, 9], 256, 512, True),                       # tiny layer shape, gate/up as one GEMM
     ([0, 1, 31, 32, 33, 64, 65, 130, 0], 512, 256, True),  # ragged groups, empty groups, tails
@@ -204,29 +210,60 @@ def _run_gemm_none(A, Bs, off, A_rows, R, label):
     ([7, 25], 1024, 512, False),                          # K split 4 ways
     ([0, 0, 0], 256, 256, False),                         # no rows at all
     ([300], 256, 768, True),                              # one big group: several row chunks
+    ([33] * 250 + [0, 64, 5] + [20] * 10, 256, 1024, True),  # enough groups for 4 tiles per wave
 ])
-def test_gemm_none_shapes(sizes, K, N, gather):
+def test_gemm_none_shapes(sizes, K, N, gather, packed):
     A, Bs, off, A_rows, R = _gemm_case(sizes, K, N, gather, seed=sum(sizes) + K + N)
-    _run_gemm_none(A, Bs, off, A_rows, R, f"sizes={sizes}")
+    _run_gemm_none(A, Bs, off, A_rows, R, f"sizes={sizes}", packed)
 
 
-def test_gemm_none_decode_grouped_gemm_full():
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
+def test_gemm_none_decode_grouped_gemm_full(packed):
     """8 groups x 32 rows, K 6144, N 2048, NONE epilogue -- the single grouped GEMM."""
     G = synth.GEMM_DECODE
     A = oracle.quantize_bf16(synth.gemm_a_bf16(G))
     Bs = synth.per_expert(lambda e: oracle.quantize(synth.gemm_b(G, e)), range(G.E))
     off = np.arange(0, (G.E + 1) * G.M, G.M, dtype=np.int32)
-    _run_gemm_none(A, Bs, off, None, G.E * G.M, "decode 8x32x6144x2048")
+    _run_gemm_none(A, Bs, off, None, G.E * G.M, "decode 8x32x6144x2048", packed)
+
+
+def _pack_reference(q: np.ndarray, sf: np.ndarray) -> np.ndarray:
+    """The packed layout written out from its definition in the header (byte moves only)."""
+    rows, half_k = q.shape
+    K = 2 * half_k
+    steps = K // 256
+    out = np.empty(rows * K * 9 // 16, np.uint8)
+    for T in range(rows // 16):
+        for s in range(steps):
+            blk = out[(T * steps + s) * 2304:(T * steps + s + 1) * 2304]
+            for l in range(64):
+                r, g = l & 15, l >> 4
+                for qq in range(2):
+                    blk[qq * 1024 + l * 16: qq * 1024 + l * 16 + 16] = q[16 * T + r, s * 128 + 32 * g + 16 * qq:][:16]
+                blk[2048 + l * 4: 2048 + l * 4 + 4] = sf[16 * T + r, s * 16 + 4 * g:][:4]
+    return out
+
+
+@pytest.mark.parametrize("rows,K", [(16, 256), (32, 256), (96, 768), (64, 1024)])
+def test_pack_weights_bit_exact(rows, K):
+    rng = np.random.default_rng(rows + K)
+    q = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    sf = rng.integers(0, 127, (rows, K // 16), dtype=np.uint8)
+    packed = torch.empty(rows * K * 9 // 16, dtype=torch.uint8, device="cuda")
+    moe.moe_pack_weights_nvfp4(dev(q), dev(sf), packed)
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), _pack_reference(q, sf))
 
 
 # ---------------------------------------------------------------------------------------
 # grouped GEMM, SwiGLU epilogue, and the requantisation that consumes it
 
-def _run_gemm_swiglu(A, Bs, off, A_rows, R, label, rows=None):
+def _run_gemm_swiglu(A, Bs, off, A_rows, R, label, rows=None, packed=False):
+    label = f"{label} {'packed' if packed else 'row-major'}"
     log(f"gemm SWIGLU {label}: E={len(Bs)} R={R}")
     Bq, Bsf, gB = stack(Bs)
     dA = moe.NVFP4Tensor(dev(A.q), dev(A.sf), dev(np.array([A.g], np.float32)))
-    dB = moe.NVFP4Tensor(dev(Bq), dev(Bsf), dev(gB))
+    dB = _weights(Bq, Bsf, gB, packed)
     act, amax = moe.grouped_gemm_alloc(dA, dB, dev(off), R, moe.MOE_EPI_SWIGLU,
                                        A_rows=dev(A_rows) if A_rows is not None else None)
     torch.cuda.synchronize()
@@ -244,10 +281,12 @@ def _run_gemm_swiglu(A, Bs, off, A_rows, R, label, rows=None):
     check_bf16(got_all[rows], ref, f"gemm SWIGLU {label} (north-star bar)")
 
 
-@pytest.mark.parametrize("sizes,K,I", [([8, 6, 9, 9], 256, 256), ([0, 17, 33, 64, 65, 1], 512, 384)])
-def test_gemm_swiglu_shapes(sizes, K, I):
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
+@pytest.mark.parametrize("sizes,K,I", [([8, 6, 9, 9], 256, 256), ([0, 17, 33, 64, 65, 1], 512, 384),
+                                       ([40] * 256 + [3, 0, 64], 256, 512)])
+def test_gemm_swiglu_shapes(sizes, K, I, packed):
     A, Bs, off, A_rows, R = _gemm_case(sizes, K, 2 * I, True, seed=7 + K + I)
-    _run_gemm_swiglu(A, Bs, off, A_rows, R, f"sizes={sizes}")
+    _run_gemm_swiglu(A, Bs, off, A_rows, R, f"sizes={sizes}", packed=packed)
 
 
 def test_requantize_bit_exact_from_partials():
@@ -290,15 +329,16 @@ def _layer_gpu(L, logits, x_bits, d1, d2):
     return plan, host_bits(out)
 
 
-def test_layer_tiny_end_to_end():
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
+def test_layer_tiny_end_to_end(packed):
     L = synth.TINY
     logits, x = synth.router_logits(L), synth.layer_activations(L)
     W1 = [oracle.quantize(synth.layer_w1(L, e)) for e in range(L.E)]
     W2 = [oracle.quantize(synth.layer_w2(L, e)) for e in range(L.E)]
     r = oracle.moe_layer(logits, x, W1, W2, L.k)
     q1, q2 = stack(W1), stack(W2)
-    d1 = moe.NVFP4Tensor(*(dev(a) for a in q1))
-    d2 = moe.NVFP4Tensor(*(dev(a) for a in q2))
+    d1 = _weights(*q1, packed)
+    d2 = _weights(*q2, packed)
     plan, got = _layer_gpu(L, logits, x, d1, d2)
     assert np.array_equal(plan.off.cpu().numpy(), r.offsets)
     assert np.array_equal(plan.xq.q.cpu().numpy(), r.xq.q)
@@ -371,8 +411,8 @@ def test_layer_deterministic():
     rng = np.random.default_rng(2)
     W1 = [oracle.quantize((rng.standard_normal((2 * L.I, L.H)) * 0.02).astype(np.float32)) for _ in range(L.E)]
     W2 = [oracle.quantize((rng.standard_normal((L.H, L.I)) * 0.02).astype(np.float32)) for _ in range(L.E)]
-    d1 = moe.NVFP4Tensor(*(dev(a) for a in stack(W1)))
-    d2 = moe.NVFP4Tensor(*(dev(a) for a in stack(W2)))
+    d1 = _weights(*stack(W1), packed=True)
+    d2 = _weights(*stack(W2), packed=True)
     logits = rng.standard_normal((L.T, L.E)).astype(np.float32)
     x = synth.bf16_bits(rng.standard_normal((L.T, L.H)).astype(np.float32))
     plan = moe.MoELayerPlan(L.T, L.E, L.k, L.H, L.I, d1, d2)
