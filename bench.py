@@ -37,7 +37,22 @@ def parse():
     ap.add_argument("--workload", default="layer_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB three times (to scale HBM "
+                         "byte counters against a kernel of known traffic) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
 def make_weights(L, moe, torch):
@@ -107,6 +122,9 @@ def cpu_baseline(L, offsets, row_src, seconds):
 
 def main():
     args = parse()
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)

@@ -389,6 +389,184 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm16_kernel(GemmParams P) {
   }
 }
 
+// Packed weights, activation tile shared through LDS (K split 1 only).  The four waves
+// of a workgroup use the same activation rows, so each K step's activation tile is
+// dequantised once per workgroup: wave w < NM turns 16-row token tile w into eight fp16
+// MFMA operand fragments per lane in LDS (double-buffered, one barrier per step), and
+// every wave reads them back with 16-byte LDS loads.  Weights stream into registers as in
+// grouped_gemm16_kernel.  NM (token tiles of the chunk) is a template parameter so that the
+// K loop is straight-line code the compiler can schedule (one dispatch per workgroup).
+struct LdsShared {
+  uint4 a[2][kTok16][8][64];   // [buffer][token tile][MFMA of step][lane]
+  float wmax[4];
+};
+
+template <int NM, int EPI>
+__device__ __forceinline__ void lds_body(const GemmParams &P, LdsShared &sh, int b, int e, int row0,
+                                         int nrows, int nt) {
+  constexpr int SPAN = 256;       // weight rows per workgroup (4 waves x 64)
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int I = P.N / 2;
+  const int steps = P.K / kKStep;
+
+  int nrow[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    if (EPI == MOE_EPI_SWIGLU) {
+      const int gate = nt * (SPAN / 2) + wv * 32 + (j & 1) * 16;
+      nrow[j] = (j >= 2) ? I + gate : gate;
+    } else {
+      nrow[j] = nt * SPAN + wv * 64 + j * 16;
+    }
+  }
+  const uint8_t *bbase[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+    bbase[j] = P.B + (static_cast<int64_t>(e) * P.N + nrow[j]) / 16 * steps * kPackBlock;
+  const uint32_t b_code_off = lane * 16, b_scale_off = 2048 + lane * 4;
+
+  const bool a_writer = wv < NM;   // wave-uniform: this wave produces token tile wv
+  const uint32_t half_k = P.K / 2, k16 = P.K / 16;
+  uint32_t aoff = 0;
+  if (a_writer) {
+    const int m = wv * 16 + r;
+    int64_t p = row0 + (m < nrows ? m : 0);
+    int64_t src = P.A_rows ? static_cast<int64_t>(P.A_rows[p]) : p;
+    src = src < 0 ? 0 : (src >= P.rows_A ? P.rows_A - 1 : src);
+    aoff = static_cast<uint32_t>(src);
+  }
+  auto load_a = [&](Frag16 &f, int s) {
+    load_frag16(f, P.A + (aoff * half_k + 32 * g + s * (kKStep / 2)),
+                P.A_sf + (aoff * k16 + 4 * g + s * (kKStep / 16)), 16);
+  };
+  auto store_a = [&](const Frag16 &f, int buf) {
+#pragma unroll
+    for (int q = 0; q < 2; q++)
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        const half8 v = dequant8(word(f.q[q], d), e4m3_to_f16(f.s, 2 * q + (d >> 1)));
+        sh.a[buf][wv][4 * q + d][lane] = __builtin_bit_cast(uint4, v);
+      }
+  };
+  auto load_b = [&](Frag16 (&f)[4], int s) {
+    const uint32_t so = static_cast<uint32_t>(s) * kPackBlock;
+#pragma unroll
+    for (int j = 0; j < 4; j++) load_frag16(f[j], bbase[j] + (so + b_code_off), bbase[j] + (so + b_scale_off), 1024);
+  };
+
+  float4v acc[4][NM];
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+#pragma unroll
+    for (int mt = 0; mt < NM; mt++) acc[j][mt] = float4v{};
+
+  Frag16 fb[4], nb[4], ra;
+  if (a_writer) {
+    load_a(ra, 0);
+    store_a(ra, 0);
+    if (steps > 1) load_a(ra, 1);
+  }
+  load_b(fb, 0);
+  __syncthreads();
+
+  for (int s = 0; s < steps; s++) {
+    const bool more = s + 1 < steps;
+    const int buf = s & 1;
+    if (more) load_b(nb, s + 1);
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        const int sb = 2 * q + (d >> 1);
+        half8 af[NM];
+#pragma unroll
+        for (int mt = 0; mt < NM; mt++) af[mt] = __builtin_bit_cast(half8, sh.a[buf][mt][4 * q + d][lane]);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const half8 bf = dequant8(word(fb[j].q[q], d), e4m3_to_f16(fb[j].s, sb));
+#pragma unroll
+          for (int mt = 0; mt < NM; mt++)
+            acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[mt], acc[j][mt], 0, 0, 0);
+        }
+      }
+    }
+    if (more) {
+      if (a_writer) {
+        store_a(ra, buf ^ 1);                    // activation tile of step s + 1
+        if (s + 2 < steps) load_a(ra, s + 2);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) fb[j] = nb[j];
+    }
+    __syncthreads();
+  }
+
+  const float gscale = (*P.A_gs) * P.B_gs[e];
+  float amax = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < NM; mt++) {
+    const int m = mt * 16 + r;
+    if (m < nrows) {
+      const int64_t p = row0 + m;
+      if (EPI == MOE_EPI_NONE) {
+        uint16_t *drow = static_cast<uint16_t *>(P.D) + p * P.N;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const uint32_t lo = f32_to_bf16(acc[j][mt][0] * gscale) |
+                              (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][1] * gscale)) << 16);
+          const uint32_t hi = f32_to_bf16(acc[j][mt][2] * gscale) |
+                              (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][3] * gscale)) << 16);
+          *reinterpret_cast<uint2 *>(drow + nrow[j] + 4 * g) = make_uint2(lo, hi);
+        }
+      } else {
+        uint16_t *drow = static_cast<uint16_t *>(P.D) + p * I;
+#pragma unroll
+        for (int jp = 0; jp < 2; jp++) {
+          uint16_t o[4];
+#pragma unroll
+          for (int c = 0; c < 4; c++) {
+            const float gate = round_bf16(acc[jp][mt][c] * gscale);
+            const float up = round_bf16(acc[2 + jp][mt][c] * gscale);
+            const float silu = gate / (1.0f + expf(-gate));
+            o[c] = f32_to_bf16(silu * up);
+            amax = fmaxf(amax, fabsf(bf16_to_f32(o[c])));
+          }
+          *reinterpret_cast<uint2 *>(drow + nrow[jp] + 4 * g) =
+              make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+        }
+      }
+    }
+  }
+  if (EPI == MOE_EPI_SWIGLU) {
+    amax = wave_max(amax);
+    if (lane == 0) sh.wmax[wv] = amax;
+    __syncthreads();
+    if (threadIdx.x == 0) P.amax_out[b] = fmaxf(fmaxf(sh.wmax[0], sh.wmax[1]), fmaxf(sh.wmax[2], sh.wmax[3]));
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void grouped_gemm16_lds_kernel(GemmParams P) {
+  __shared__ LdsShared sh;
+  const int b = blockIdx.x;
+  const int count = *P.count;
+  const int per_xcd = (count + kXcds - 1) / kXcds;
+  const int jx = b / kXcds;
+  const int w = (b % kXcds) * per_xcd + jx;
+  if (jx >= per_xcd || w >= count) {
+    if (EPI == MOE_EPI_SWIGLU && threadIdx.x == 0) P.amax_out[b] = 0.f;
+    return;
+  }
+  const int4 item = P.items[w];
+  const int nm = (item.z + 15) / 16;   // workgroup-uniform
+  if (nm <= 1) lds_body<1, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
+  else if (nm == 2) lds_body<2, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
+  else lds_body<3, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
+}
+
 // ---- the kernel ----------------------------------------------------------------
 //
 // Row-major weights, 32x32x16 fp16 MFMA.  KS: K split across the waves of a workgroup
@@ -593,7 +771,7 @@ template <int EPI>
 void launch_epi(const GemmParams &p, const GemmPlan &plan, bool packed, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(plan.grid)), block(256);
   if (packed) {
-    if (plan.ks == 1) hipLaunchKernelGGL((grouped_gemm16_kernel<1, EPI>), grid, block, 0, stream, p);
+    if (plan.ks == 1) hipLaunchKernelGGL((grouped_gemm16_lds_kernel<EPI>), grid, block, 0, stream, p);
     else if (plan.ks == 2) hipLaunchKernelGGL((grouped_gemm16_kernel<2, EPI>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((grouped_gemm16_kernel<4, EPI>), grid, block, 0, stream, p);
   } else {
