@@ -86,6 +86,47 @@ def make_weights(L, moe, torch):
     return out["W1"], out["W2"]
 
 
+def grouped_gemm_decode(moe, torch, steps: int, copies: int = 8) -> dict:
+    """The single grouped GEMM at decode shape (8 groups x 32 rows, K 6144, N 2048, NONE
+    epilogue) on packed weights.  `copies` distinct weight copies (8 x 56.6 MB, more than
+    the 256 MB Infinity Cache) are cycled so that every launch streams its weights from HBM."""
+    import synth
+    G = synth.GEMM_DECODE
+    dev = torch.device("cuda")
+    wq = torch.empty(G.E, G.N, G.K // 2, dtype=torch.uint8, device=dev)
+    wsf = torch.empty(G.E, G.N, G.K // 16, dtype=torch.uint8, device=dev)
+    wgs = torch.empty(G.E, dtype=torch.float32, device=dev)
+    for e in range(G.E):
+        w = torch.from_numpy(synth.gemm_b(G, e)).to(dev)
+        moe.moe_quantize_nvfp4(w, wq[e], wsf[e], wgs[e:e + 1], moe.MOE_GS_DYNAMIC)
+    packed = moe.pack_weights(moe.NVFP4Tensor(wq, wsf, wgs))
+    Ws = [packed] + [moe.PackedWeights(packed.data.clone(), wgs, G.N, G.K) for _ in range(copies - 1)]
+    a_bits = torch.from_numpy(synth.gemm_a_bf16(G).view(np.int16)).to(dev).view(torch.bfloat16)
+    A = moe.quantize_alloc(a_bits)
+    off = torch.arange(0, (G.E + 1) * G.M, G.M, dtype=torch.int32, device=dev)
+    R = G.E * G.M
+    D = torch.empty(R, G.N, dtype=torch.bfloat16, device=dev)
+    args = [moe._gemm_args_for(A, W, off, R, moe.MOE_EPI_NONE, D, None) for W in Ws]
+    ws = moe._ws(moe.moe_grouped_gemm_nvfp4_workspace(args[0]), dev)
+    for a in args:
+        moe.moe_grouped_gemm_nvfp4(a, ws)
+    torch.cuda.synchronize()
+    n = max(steps, 10) * copies
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        moe.moe_grouped_gemm_nvfp4(args[i % copies], ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    w_bytes = G.E * G.N * (G.K // 2 + G.K // 16)
+    alg = w_bytes + R * (G.K // 2 + G.K // 16) + R * G.N * 2
+    flops = 2.0 * R * G.N * G.K
+    return {"workload": G.name, "avg_launch_us": round(us, 2), "tflops": round(flops / us / 1e6, 2),
+            "alg_bytes_per_launch": alg, "GBps": round(alg / us / 1e3, 1),
+            "hbm_frac": round(alg / us / 1e3 / HBM_PEAK_GBPS, 4), "weight_copies_rotated": copies}
+
+
 def cpu_baseline(L, offsets, row_src, seconds):
     """The oracle's grouped GEMMs (gate/up then down) over the routed rows of the first
     experts, one expert at a time until `seconds` of CPU time is spent; FLOPs / time."""
@@ -208,6 +249,8 @@ def main():
         "weight_hbm_frac": round(weight_gbps / HBM_PEAK_GBPS, 4),
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
     }
+    if L is synth.LAYER_DECODE:
+        rec["grouped_gemm_decode_8x32"] = grouped_gemm_decode(moe, torch, args.steps)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(L, off, plan.row_src.cpu().numpy(), args.cpu_baseline_seconds)
     print(json.dumps(rec), flush=True)

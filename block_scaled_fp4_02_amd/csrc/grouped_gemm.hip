@@ -119,6 +119,13 @@ __device__ __forceinline__ half8 dequant8(uint32_t codes, _Float16 s) {
   return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// E4M3FN bytes (2*hi, 2*hi + 1) of a dword -> two fp16 (exact: every E4M3 value is an fp16
+// value; the converter's scale operand is 1.0, a power of two, which it applies exactly).
+__device__ __forceinline__ half2v e4m3x2_to_f16(uint32_t w, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+            : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+}
+
 // E4M3FN byte `sel` (0..3) of a dword -> fp16 (exact: every E4M3 value is an fp16 value).
 // `sel` is a constant once the caller's loops are unrolled.
 __device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t w, int sel) {
@@ -202,8 +209,9 @@ __device__ __forceinline__ void load_frag16(Frag16 &f, const uint8_t *codes, con
   f.s = *reinterpret_cast<const uint32_t *>(scales);
 }
 
-template <int KS, int EPI>
-__global__ __launch_bounds__(256, 2) void grouped_gemm16_kernel(GemmParams P) {
+template <int NM, int KS, int EPI>
+__device__ __forceinline__ void ks_body(const GemmParams &P, float *red, float *wmax, int b, int e,
+                                        int row0, int nrows, int nt) {
   constexpr int NG = 4 / KS;
   constexpr int SPAN = NG * 64;   // weight rows per workgroup
   const int lane = threadIdx.x & 63;
@@ -212,18 +220,6 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm16_kernel(GemmParams P) {
   const int kq = wv / NG;
   const int r = lane & 15;        // row within a 16-row tile
   const int g = lane >> 4;        // K group of the lane
-
-  const int b = blockIdx.x;
-  const int count = *P.count;
-  const int per_xcd = (count + kXcds - 1) / kXcds;
-  const int jx = b / kXcds;
-  const int w = (b % kXcds) * per_xcd + jx;
-  if (jx >= per_xcd || w >= count) {
-    if (EPI == MOE_EPI_SWIGLU && threadIdx.x == 0) P.amax_out[b] = 0.f;
-    return;
-  }
-  const int4 item = P.items[w];
-  const int e = item.x, row0 = item.y, nrows = item.z, nt = item.w;
   const int I = P.N / 2;
   const int steps = P.K / kKStep;
 
@@ -244,13 +240,12 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm16_kernel(GemmParams P) {
   for (int j = 0; j < 4; j++)
     bbase[j] = P.B + (static_cast<int64_t>(e) * P.N + nrow[j]) / 16 * steps * kPackBlock;
   const uint32_t b_code_off = lane * 16, b_scale_off = 2048 + lane * 4;
-  // token rows of the (up to four) 16-row tiles of the chunk: 32-bit offsets into A
+  // token rows of the NM 16-row tiles of the chunk: 32-bit offsets into A
   // (rows_A * K / 2 < 2^32 is checked on the host)
-  const int nm = (nrows + 15) / 16;
   const uint32_t half_k = P.K / 2, k16 = P.K / 16;
-  uint32_t aoff[kTok16];
+  uint32_t aoff[NM];
 #pragma unroll
-  for (int mt = 0; mt < kTok16; mt++) {
+  for (int mt = 0; mt < NM; mt++) {
     const int m = mt * 16 + r;
     int64_t p = row0 + (m < nrows ? m : 0);
     int64_t src = P.A_rows ? static_cast<int64_t>(P.A_rows[p]) : p;
@@ -258,24 +253,23 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm16_kernel(GemmParams P) {
     aoff[mt] = static_cast<uint32_t>(src);
   }
 
-  float4v acc[4][kTok16];
+  float4v acc[4][NM];
 #pragma unroll
   for (int j = 0; j < 4; j++)
 #pragma unroll
-    for (int mt = 0; mt < kTok16; mt++) acc[j][mt] = float4v{};
+    for (int mt = 0; mt < NM; mt++) acc[j][mt] = float4v{};
 
   const int s_begin = kq * (steps / KS);
   const int iters = steps / KS;
-  Frag16 fb[4], fa[kTok16], nb[4], na[kTok16];
+  Frag16 fb[4], fa[NM], nb[4], na[NM];
   auto load_b = [&](Frag16 (&f)[4], int s) {
     const uint32_t so = static_cast<uint32_t>(s) * kPackBlock;
 #pragma unroll
     for (int j = 0; j < 4; j++) load_frag16(f[j], bbase[j] + (so + b_code_off), bbase[j] + (so + b_scale_off), 1024);
   };
-  auto load_a = [&](Frag16 (&f)[kTok16], int s) {
+  auto load_a = [&](Frag16 (&f)[NM], int s) {
 #pragma unroll
-    for (int mt = 0; mt < kTok16; mt++)
-      if (mt < nm)
+    for (int mt = 0; mt < NM; mt++)
         load_frag16(f[mt], P.A + (aoff[mt] * half_k + 32 * g + s * (kKStep / 2)),
                     P.A_sf + (aoff[mt] * k16 + 4 * g + s * (kKStep / 16)), 16);
   };
@@ -290,19 +284,23 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm16_kernel(GemmParams P) {
     }
 #pragma unroll
     for (int q = 0; q < 2; q++) {
+      half2v bsc[4], asc[NM];
+#pragma unroll
+      for (int j = 0; j < 4; j++) bsc[j] = e4m3x2_to_f16(fb[j].s, q == 1);
+#pragma unroll
+      for (int mt = 0; mt < NM; mt++) asc[mt] = e4m3x2_to_f16(fa[mt].s, q == 1);
 #pragma unroll
       for (int d = 0; d < 4; d++) {
-        const int sb = 2 * q + (d >> 1);
-        half8 af[kTok16];
+        half8 af[NM];
 #pragma unroll
-        for (int mt = 0; mt < kTok16; mt++)
-          if (mt < nm) af[mt] = dequant8(word(fa[mt].q[q], d), e4m3_to_f16(fa[mt].s, sb));
+        for (int mt = 0; mt < NM; mt++)
+          af[mt] = dequant8(word(fa[mt].q[q], d), asc[mt][d >> 1]);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const half8 bf = dequant8(word(fb[j].q[q], d), e4m3_to_f16(fb[j].s, sb));
+          const half8 bf = dequant8(word(fb[j].q[q], d), bsc[j][d >> 1]);
 #pragma unroll
-          for (int mt = 0; mt < kTok16; mt++)
-            if (mt < nm) acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[mt], acc[j][mt], 0, 0, 0);
+          for (int mt = 0; mt < NM; mt++)
+            acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[mt], acc[j][mt], 0, 0, 0);
         }
       }
     }
@@ -310,20 +308,18 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm16_kernel(GemmParams P) {
 #pragma unroll
       for (int j = 0; j < 4; j++) fb[j] = nb[j];
 #pragma unroll
-      for (int mt = 0; mt < kTok16; mt++)
-        if (mt < nm) fa[mt] = na[mt];
+      for (int mt = 0; mt < NM; mt++) fa[mt] = na[mt];
     }
   }
 
   if constexpr (KS > 1) {
     constexpr int TILE = 4 * kTok16 * 4 * 64;
-    __shared__ float red[(KS - 1) * NG * TILE];
     float *mine = red + ((kq - 1) * NG + ng) * TILE;
     if (kq > 0) {
 #pragma unroll
       for (int j = 0; j < 4; j++)
 #pragma unroll
-        for (int mt = 0; mt < kTok16; mt++)
+        for (int mt = 0; mt < NM; mt++)
 #pragma unroll
           for (int i = 0; i < 4; i++) mine[((j * kTok16 + mt) * 4 + i) * 64 + lane] = acc[j][mt][i];
     }
@@ -334,7 +330,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm16_kernel(GemmParams P) {
 #pragma unroll
         for (int j = 0; j < 4; j++)
 #pragma unroll
-          for (int mt = 0; mt < kTok16; mt++)
+          for (int mt = 0; mt < NM; mt++)
 #pragma unroll
             for (int i = 0; i < 4; i++) acc[j][mt][i] += src[((j * kTok16 + mt) * 4 + i) * 64 + lane];
       }
@@ -346,9 +342,9 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm16_kernel(GemmParams P) {
   float amax = 0.f;
   if (kq == 0) {
 #pragma unroll
-    for (int mt = 0; mt < kTok16; mt++) {
+    for (int mt = 0; mt < NM; mt++) {
       const int m = mt * 16 + r;
-      if (mt < nm && m < nrows) {
+      if (m < nrows) {
         const int64_t p = row0 + m;
         if (EPI == MOE_EPI_NONE) {
           uint16_t *drow = static_cast<uint16_t *>(P.D) + p * P.N;
@@ -381,12 +377,32 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm16_kernel(GemmParams P) {
     }
   }
   if (EPI == MOE_EPI_SWIGLU) {
-    __shared__ float wmax[4];
     amax = wave_max(amax);
     if (lane == 0) wmax[wv] = amax;
     __syncthreads();
     if (threadIdx.x == 0) P.amax_out[b] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   }
+}
+
+template <int KS, int EPI>
+__global__ __launch_bounds__(256, 2) void grouped_gemm16_kernel(GemmParams P) {
+  constexpr int TILE = 4 * kTok16 * 4 * 64;
+  __shared__ float red[KS > 1 ? (KS - 1) * (4 / KS) * TILE : 1];
+  __shared__ float wmax[4];
+  const int b = blockIdx.x;
+  const int count = *P.count;
+  const int per_xcd = (count + kXcds - 1) / kXcds;
+  const int jx = b / kXcds;
+  const int w = (b % kXcds) * per_xcd + jx;
+  if (jx >= per_xcd || w >= count) {
+    if (EPI == MOE_EPI_SWIGLU && threadIdx.x == 0) P.amax_out[b] = 0.f;
+    return;
+  }
+  const int4 item = P.items[w];
+  const int nm = (item.z + 15) / 16;   // workgroup-uniform
+  if (nm <= 1) ks_body<1, KS, EPI>(P, red, wmax, b, item.x, item.y, item.z, item.w);
+  else if (nm == 2) ks_body<2, KS, EPI>(P, red, wmax, b, item.x, item.y, item.z, item.w);
+  else ks_body<3, KS, EPI>(P, red, wmax, b, item.x, item.y, item.z, item.w);
 }
 
 // Packed weights, activation tile shared through LDS (K split 1 only).  The four waves
@@ -444,12 +460,14 @@ __device__ __forceinline__ void lds_body(const GemmParams &P, LdsShared &sh, int
   };
   auto store_a = [&](const Frag16 &f, int buf) {
 #pragma unroll
-    for (int q = 0; q < 2; q++)
+    for (int q = 0; q < 2; q++) {
+      const half2v sc = e4m3x2_to_f16(f.s, q == 1);
 #pragma unroll
       for (int d = 0; d < 4; d++) {
-        const half8 v = dequant8(word(f.q[q], d), e4m3_to_f16(f.s, 2 * q + (d >> 1)));
+        const half8 v = dequant8(word(f.q[q], d), sc[d >> 1]);
         sh.a[buf][wv][4 * q + d][lane] = __builtin_bit_cast(uint4, v);
       }
+    }
   };
   auto load_b = [&](Frag16 (&f)[4], int s) {
     const uint32_t so = static_cast<uint32_t>(s) * kPackBlock;
@@ -478,15 +496,17 @@ __device__ __forceinline__ void lds_body(const GemmParams &P, LdsShared &sh, int
     if (more) load_b(nb, s + 1);
 #pragma unroll
     for (int q = 0; q < 2; q++) {
+      half2v bsc[4];   // scales of blocks 2q, 2q + 1 of each tile
+#pragma unroll
+      for (int j = 0; j < 4; j++) bsc[j] = e4m3x2_to_f16(fb[j].s, q == 1);
 #pragma unroll
       for (int d = 0; d < 4; d++) {
-        const int sb = 2 * q + (d >> 1);
         half8 af[NM];
 #pragma unroll
         for (int mt = 0; mt < NM; mt++) af[mt] = __builtin_bit_cast(half8, sh.a[buf][mt][4 * q + d][lane]);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const half8 bf = dequant8(word(fb[j].q[q], d), e4m3_to_f16(fb[j].s, sb));
+          const half8 bf = dequant8(word(fb[j].q[q], d), bsc[j][d >> 1]);
 #pragma unroll
           for (int mt = 0; mt < NM; mt++)
             acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[mt], acc[j][mt], 0, 0, 0);
@@ -572,8 +592,9 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm16_lds_kernel(GemmParams P
 // Row-major weights, 32x32x16 fp16 MFMA.  KS: K split across the waves of a workgroup
 // (1, 2, 4); NG = 4 / KS wave groups along N; each wave owns two 32-row weight tiles (with
 // the SwiGLU epilogue a (gate, up) pair), so a workgroup covers NG * 64 weight rows.
-template <int KS, int EPI>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmParams P) {
+template <int NM, int KS, int EPI>
+__device__ __forceinline__ void rm_body(const GemmParams &P, float *red, float *wmax, int b, int e,
+                                        int row0, int nrows, int nt) {
   constexpr int TPW = 2;
   constexpr int NG = 4 / KS;
   constexpr int SPAN = NG * TPW * 32;                  // weight rows per workgroup
@@ -584,19 +605,6 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmParams P) {
   const int kq = wv / NG;
   const int r = lane & 31;    // row within a 32-row tile
   const int h = lane >> 5;    // lane half: which 128 of each 256 K elements
-
-  // work item for this workgroup (contiguous ranges per XCD)
-  const int b = blockIdx.x;
-  const int count = *P.count;
-  const int per_xcd = (count + kXcds - 1) / kXcds;
-  const int jx = b / kXcds;
-  const int w = (b % kXcds) * per_xcd + jx;
-  if (jx >= per_xcd || w >= count) {
-    if (EPI == MOE_EPI_SWIGLU && threadIdx.x == 0) P.amax_out[b] = 0.f;
-    return;
-  }
-  const int4 item = P.items[w];
-  const int e = item.x, row0 = item.y, nrows = item.z, nt = item.w;
   const int I = P.N / 2;
   const int steps = P.K / kKStep;
 
@@ -625,7 +633,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmParams P) {
   const int64_t b_scale_step = kKStep / 16;
 
   // activation rows of the (one or two) 32-row tiles of the chunk
-  const int nm = nrows > 32 ? 2 : 1;
+  constexpr int nm = NM;
   const uint8_t *aq[2];
   const uint8_t *as[2];
 #pragma unroll
@@ -691,7 +699,6 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmParams P) {
   // K split across waves: partial tiles added in LDS in a fixed order
   if constexpr (KS > 1) {
     constexpr int TILE = TPW * 2 * 16 * 64;
-    __shared__ float red[(KS - 1) * NG * TILE];
     float *mine = red + ((kq - 1) * NG + ng) * TILE;
     if (kq > 0) {
 #pragma unroll
@@ -759,12 +766,30 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmParams P) {
     }
   }
   if (EPI == MOE_EPI_SWIGLU) {
-    __shared__ float wmax[4];
     amax = wave_max(amax);
     if (lane == 0) wmax[wv] = amax;
     __syncthreads();
     if (threadIdx.x == 0) P.amax_out[b] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   }
+}
+
+template <int KS, int EPI>
+__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmParams P) {
+  constexpr int TILE = 2 * 2 * 16 * 64;
+  __shared__ float red[KS > 1 ? (KS - 1) * (4 / KS) * TILE : 1];
+  __shared__ float wmax[4];
+  const int b = blockIdx.x;
+  const int count = *P.count;
+  const int per_xcd = (count + kXcds - 1) / kXcds;
+  const int jx = b / kXcds;
+  const int w = (b % kXcds) * per_xcd + jx;
+  if (jx >= per_xcd || w >= count) {
+    if (EPI == MOE_EPI_SWIGLU && threadIdx.x == 0) P.amax_out[b] = 0.f;
+    return;
+  }
+  const int4 item = P.items[w];
+  if (item.z > 32) rm_body<2, KS, EPI>(P, red, wmax, b, item.x, item.y, item.z, item.w);
+  else rm_body<1, KS, EPI>(P, red, wmax, b, item.x, item.y, item.z, item.w);
 }
 
 template <int EPI>

@@ -71,12 +71,14 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return __uint_as_float((((c >> 3) + 120u) << 23) | ((c & 7u) << 20));
 }
 
-// E2M1 magnitude code for u in [0, 6], ties to the even code.
+// E2M1 magnitude code for u in [0, 6], ties to the even code.  Below 1 the E2M1 values are
+// the multiples of 0.5 (code = 2u rounded to nearest even); from 1 up they have one mantissa
+// bit, so the binary32 mantissa is rounded to one bit and the exponent rebiased (127 -> 1).
 __device__ __forceinline__ uint32_t e2m1_rne(float u) {
-  return static_cast<uint32_t>(u > 0.25f) + static_cast<uint32_t>(u >= 0.75f) +
-         static_cast<uint32_t>(u > 1.25f) + static_cast<uint32_t>(u >= 1.75f) +
-         static_cast<uint32_t>(u > 2.5f) + static_cast<uint32_t>(u >= 3.5f) +
-         static_cast<uint32_t>(u > 5.0f);
+  if (u < 1.0f) return static_cast<uint32_t>(rintf(u * 2.0f));
+  uint32_t b = __float_as_uint(u);
+  b += 0x1fffffu + ((b >> 22) & 1u);
+  return (b >> 22) - (126u << 1);
 }
 
 __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, int x_dtype,
@@ -154,8 +156,8 @@ hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t C, 
   const int dynamic = gs_mode == MOE_GS_DYNAMIC;
   int nparts = 0;
   if (dynamic) {
-    const int64_t work = amax_in ? n_amax_in : n;
-    int64_t g = (work + 256 * 32 - 1) / (256 * 32);
+    // partial maxima: ~4 per thread; tensor data: ~32 elements per thread
+    const int64_t g = amax_in ? (n_amax_in + 1023) / 1024 : (n + 256 * 32 - 1) / (256 * 32);
     nparts = static_cast<int>(g < 1 ? 1 : (g > kAmaxParts ? kAmaxParts : g));
     hipLaunchKernelGGL(amax_kernel, dim3(nparts), dim3(256), 0, stream, x, x_dtype, n, amax_in,
                        n_amax_in, parts);
