@@ -11,6 +11,10 @@ namespace moe {
 constexpr int kWave = 64;   // CDNA wavefront width
 constexpr int kXcds = 8;    // MI355X: workgroups are dispatched round-robin over 8 XCDs
 
+// Largest operand (packed weights of one expert, activation codes) that the packed-layout
+// grouped GEMM addresses through one range-checked buffer descriptor.
+constexpr int64_t kMaxPackedBufBytes = (int64_t(1) << 31) - 4096;
+
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float16v __attribute__((ext_vector_type(16)));

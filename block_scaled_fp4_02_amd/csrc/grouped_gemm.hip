@@ -209,6 +209,27 @@ __device__ __forceinline__ void load_frag16(Frag16 &f, const uint8_t *codes, con
   f.s = *reinterpret_cast<const uint32_t *>(scales);
 }
 
+// Buffer resources (raw, byte-addressed) with hardware range checking: an access at an
+// offset at or past `bytes` returns zeros and reads no memory.  Ranges stay below kOob, so
+// kOob plus any in-range offset is out of range without wrapping.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOob = 0x80000000u;
+static_assert(kMaxPackedBufBytes + 4096 <= kOob, "buffer ranges must stay below the out-of-range offset");
+
+__device__ __forceinline__ BufRsrc make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ void load_frag16_buf(Frag16 &f, BufRsrc rc, uint32_t code_off, uint32_t qs, BufRsrc rs,
+                                                uint32_t scale_off) {
+  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rc, code_off, 0, 0);
+  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rc, code_off + qs, 0, 0);
+  f.q[0] = make_uint4(a.x, a.y, a.z, a.w);
+  f.q[1] = make_uint4(b.x, b.y, b.z, b.w);
+  f.s = __builtin_amdgcn_raw_buffer_load_b32(rs, scale_off, 0, 0);
+}
+
 template <int NM, int KS, int EPI>
 __device__ __forceinline__ void ks_body(const GemmParams &P, float *red, float *wmax, int b, int e,
                                         int row0, int nrows, int nt) {
@@ -438,25 +459,38 @@ __device__ __forceinline__ void lds_body(const GemmParams &P, LdsShared &sh, int
       nrow[j] = nt * SPAN + wv * 64 + j * 16;
     }
   }
-  const uint8_t *bbase[4];
+  // All operand loads are buffer loads through range-checked descriptors (one over this
+  // expert's packed weights, two over the activation codes and scales).  A load past the
+  // last K step, or by a wave that produces no activation tile, gets an offset beyond the
+  // range: it returns zeros without touching memory.  So every step issues the same loads
+  // unconditionally, and the compiler can count the loads still in flight exactly (a load
+  // behind a branch makes it wait for all of them).
+  const uint32_t expert_bytes = static_cast<uint32_t>(P.N / 16) * steps * kPackBlock;
+  const BufRsrc rb = make_rsrc(P.B + static_cast<int64_t>(e) * expert_bytes, expert_bytes);
+  uint32_t b_code[4], b_scale[4];
 #pragma unroll
-  for (int j = 0; j < 4; j++)
-    bbase[j] = P.B + (static_cast<int64_t>(e) * P.N + nrow[j]) / 16 * steps * kPackBlock;
-  const uint32_t b_code_off = lane * 16, b_scale_off = 2048 + lane * 4;
+  for (int j = 0; j < 4; j++) {
+    b_code[j] = static_cast<uint32_t>(nrow[j] / 16) * steps * kPackBlock + lane * 16;
+    b_scale[j] = static_cast<uint32_t>(nrow[j] / 16) * steps * kPackBlock + 2048 + lane * 4;
+  }
 
   const bool a_writer = wv < NM;   // wave-uniform: this wave produces token tile wv
   const uint32_t half_k = P.K / 2, k16 = P.K / 16;
-  uint32_t aoff = 0;
+  const BufRsrc ra_codes = make_rsrc(P.A, static_cast<uint32_t>(P.rows_A * half_k));
+  const BufRsrc ra_scales = make_rsrc(P.A_sf, static_cast<uint32_t>(P.rows_A * k16));
+  uint32_t a_code = 0, a_scale = 0;
   if (a_writer) {
     const int m = wv * 16 + r;
     int64_t p = row0 + (m < nrows ? m : 0);
     int64_t src = P.A_rows ? static_cast<int64_t>(P.A_rows[p]) : p;
     src = src < 0 ? 0 : (src >= P.rows_A ? P.rows_A - 1 : src);
-    aoff = static_cast<uint32_t>(src);
+    a_code = static_cast<uint32_t>(src) * half_k + 32 * g;
+    a_scale = static_cast<uint32_t>(src) * k16 + 4 * g;
   }
   auto load_a = [&](Frag16 &f, int s) {
-    load_frag16(f, P.A + (aoff * half_k + 32 * g + s * (kKStep / 2)),
-                P.A_sf + (aoff * k16 + 4 * g + s * (kKStep / 16)), 16);
+    const bool v = a_writer && s < steps;
+    load_frag16_buf(f, ra_codes, v ? a_code + s * (kKStep / 2) : kOob, 16, ra_scales,
+                    v ? a_scale + s * (kKStep / 16) : kOob);
   };
   auto store_a = [&](const Frag16 &f, int buf) {
 #pragma unroll
@@ -470,9 +504,9 @@ __device__ __forceinline__ void lds_body(const GemmParams &P, LdsShared &sh, int
     }
   };
   auto load_b = [&](Frag16 (&f)[4], int s) {
-    const uint32_t so = static_cast<uint32_t>(s) * kPackBlock;
+    const uint32_t so = s < steps ? static_cast<uint32_t>(s) * kPackBlock : kOob;
 #pragma unroll
-    for (int j = 0; j < 4; j++) load_frag16(f[j], bbase[j] + (so + b_code_off), bbase[j] + (so + b_scale_off), 1024);
+    for (int j = 0; j < 4; j++) load_frag16_buf(f[j], rb, b_code[j] + so, 1024, rb, b_scale[j] + so);
   };
 
   float4v acc[4][NM];
@@ -481,19 +515,20 @@ __device__ __forceinline__ void lds_body(const GemmParams &P, LdsShared &sh, int
 #pragma unroll
     for (int mt = 0; mt < NM; mt++) acc[j][mt] = float4v{};
 
-  Frag16 fb[4], nb[4], ra;
-  if (a_writer) {
-    load_a(ra, 0);
-    store_a(ra, 0);
-    if (steps > 1) load_a(ra, 1);
-  }
-  load_b(fb, 0);
+  // Weight fragments rotate through three register sets: the loads of step s + 2 are in
+  // flight while step s computes.  Loads are issued in the same order in the prologue as in
+  // every step (weights of a step, then its activation tile).
+  Frag16 f0[4], f1[4], f2[4], ra, ra0;
+  load_b(f0, 0);
+  load_a(ra0, 0);
+  load_b(f1, 1);
+  load_a(ra, 1);
+  if (a_writer) store_a(ra0, 0);
   __syncthreads();
 
-  for (int s = 0; s < steps; s++) {
-    const bool more = s + 1 < steps;
+  auto step = [&](const Frag16 (&fb)[4], Frag16 (&fl)[4], int s) {
     const int buf = s & 1;
-    if (more) load_b(nb, s + 1);
+    load_b(fl, s + 2);
 #pragma unroll
     for (int q = 0; q < 2; q++) {
       half2v bsc[4];   // scales of blocks 2q, 2q + 1 of each tile
@@ -513,16 +548,18 @@ __device__ __forceinline__ void lds_body(const GemmParams &P, LdsShared &sh, int
         }
       }
     }
-    if (more) {
-      if (a_writer) {
-        store_a(ra, buf ^ 1);                    // activation tile of step s + 1
-        if (s + 2 < steps) load_a(ra, s + 2);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; j++) fb[j] = nb[j];
-    }
+    if (a_writer && s + 1 < steps) store_a(ra, buf ^ 1);   // activation tile of step s + 1
+    load_a(ra, s + 2);
     __syncthreads();
+  };
+  int s = 0;
+  for (; s + 3 <= steps; s += 3) {
+    step(f0, f2, s);
+    step(f1, f0, s + 1);
+    step(f2, f1, s + 2);
   }
+  if (s < steps) step(f0, f2, s);
+  if (s + 1 < steps) step(f1, f0, s + 1);
 
   const float gscale = (*P.A_gs) * P.B_gs[e];
   float amax = 0.f;

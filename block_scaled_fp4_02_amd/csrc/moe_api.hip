@@ -26,8 +26,11 @@ moe_status check_gemm(const moe_gemm_args *a, bool need_pointers) {
   if (a->K % 16 != 0) return MOE_ERR_SHAPE;
   if (a->K % 256 != 0 || a->N % 256 != 0) return MOE_ERR_UNSUPPORTED;
   if (a->R > 0 && a->rows_A < 1) return MOE_ERR_SHAPE;
-  // the packed kernel addresses A with 32-bit byte offsets
-  if (a->B_layout == MOE_LAYOUT_PACKED && a->rows_A * (a->K / 2) >= (int64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;
+  // the packed kernel addresses the activation codes and each expert's packed weights
+  // through 32-bit range-checked buffer descriptors
+  if (a->B_layout == MOE_LAYOUT_PACKED &&
+      (a->rows_A * (a->K / 2) > kMaxPackedBufBytes || static_cast<int64_t>(a->N) * a->K / 16 * 9 > kMaxPackedBufBytes))
+    return MOE_ERR_UNSUPPORTED;
   // item indices, row indices and workgroup counts stay in 32 bits
   const GemmPlan plan = plan_gemm(*a);
   if (plan.grid >= (int64_t(1) << 31) || static_cast<int64_t>(a->E) * a->N >= (int64_t(1) << 40))

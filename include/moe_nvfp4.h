@@ -145,8 +145,10 @@ moe_status moe_quantize_nvfp4(const void *x, int x_dtype, int64_t rows, int64_t 
  * Rows p >= expert_offsets[E] of D are not written.
  * B_layout MOE_LAYOUT_ROWMAJOR: B / B_sf as above.  MOE_LAYOUT_PACKED: B is the output of
  * moe_pack_weights_nvfp4 for the E*N weight rows (B_sf is ignored and may be NULL); this is
- * the layout the decode kernels stream at full HBM rate.
- * Supported: K % 256 == 0, N % 256 == 0, 1 <= E <= 65536, 0 <= R < 2^31.
+ * the layout the decode kernels stream with fully coalesced loads.
+ * Supported: K % 256 == 0, N % 256 == 0, 1 <= E <= 65536, 0 <= R < 2^31; with the packed
+ * layout also rows_A * K / 2 <= 2^31 - 4096 and N * K * 9 / 16 <= 2^31 - 4096 (one expert's
+ * packed weights), MOE_ERR_UNSUPPORTED otherwise.
  * moe_grouped_gemm_nvfp4_can_implement() returns MOE_OK exactly when the
  * launch is supported; a supported launch then cannot fail on its
  * configuration.  ws: moe_grouped_gemm_nvfp4_workspace(args) bytes.
