@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build", "moe_nvfp4")
 LIB_PATH = os.path.join(PKG, "libmoe_nvfp4.so")
-SOURCES = ["route_permute.hip", "quantize.hip", "grouped_gemm.hip", "finalize.hip", "moe_api.hip"]
+SOURCES = ["route_permute.hip", "quantize.hip", "grouped_gemm.hip", "gemm_lds.hip", "gemm_ksplit.hip",
+           "gemm_rowmajor.hip", "finalize.hip", "moe_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH_FLAGS = ["--offload-arch=gfx950"]

@@ -60,6 +60,7 @@ hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t C, 
 size_t quantize_ws_bytes(int64_t rows, int64_t C);
 
 struct GemmPlan {
+  int kernel;        // kernel family (gemm::Kernel)
   int chunk_rows;    // rows per work item
   int ks;            // K split across the waves of a workgroup: 1, 2 or 4
   int n_tile;        // weight rows (output columns of y) per workgroup

@@ -1,0 +1,161 @@
+// Device-side pieces shared by the grouped NVFP4 GEMM kernels (gemm_*.hip): kernel
+// parameters, the work-item mapping, operand fragments and their loads, and the exact
+// NVFP4 -> fp16 dequantisation.  Not part of the ABI.
+//
+// Exactness: an E2M1 element times its E4M3 block scale has at most 6 significant bits and
+// lies in [2^-10, 2688], so it is exact in fp16.  Both operands are dequantised that way
+// (hardware FP4 -> fp16 conversion, then a packed fp16 multiply by the block scale), so a
+// plain fp16 MFMA with fp32 accumulation sums exact products; the two global scales
+// multiply the fp32 result in the epilogue.  (gfx950's block-scaled FP4 MFMA takes
+// power-of-two scales per 32 elements and cannot carry an E4M3 scale per 16.)
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+namespace gemm {
+
+constexpr int kKStep = 256;       // K elements per step of every kernel
+constexpr int kPackBlock = 2304;  // bytes of one (16-row tile, K step) block of packed weights
+
+struct Params {
+  const uint8_t *A;
+  const uint8_t *A_sf;
+  const float *A_gs;
+  const int32_t *A_rows;
+  int64_t rows_A;
+  const uint8_t *B;
+  const uint8_t *B_sf;
+  const float *B_gs;
+  int E, N, K;
+  void *D;
+  float *amax_out;
+  const int4 *items;   // (expert, first row, rows, n tile), from the schedule kernel
+  const int *count;    // number of valid items
+};
+
+// Work item of workgroup b, or false if it has none.  Workgroup b runs on XCD b % 8, so
+// the items are dealt to XCDs in contiguous ranges: neighbouring items (the n tiles and row
+// chunks of one expert) share that XCD's L2.
+__device__ __forceinline__ bool item_for_block(const Params &P, int b, int4 &item) {
+  const int count = *P.count;
+  const int per_xcd = (count + kXcds - 1) / kXcds;
+  const int jx = b / kXcds;
+  const int w = (b % kXcds) * per_xcd + jx;
+  if (jx >= per_xcd || w >= count) return false;
+  item = P.items[w];
+  return true;
+}
+
+// ---- dequantisation ------------------------------------------------------------------
+
+// 8 E2M1 codes (one dword, element 2i in the low nibble of byte i) times scale s -> 8 fp16.
+__device__ __forceinline__ half8 dequant8(uint32_t codes, _Float16 s) {
+  const half2v sc = {s, s};
+  const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * sc;
+  const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * sc;
+  const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * sc;
+  const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * sc;
+  return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// E4M3FN bytes (2*hi, 2*hi + 1) of a dword -> two fp16 (exact: every E4M3 value is an fp16
+// value; the converter's scale operand is 1.0, a power of two, which it applies exactly).
+__device__ __forceinline__ half2v e4m3x2_to_f16(uint32_t w, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+            : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+}
+
+// E4M3FN byte `sel` (0..3) of a dword -> fp16 (exact: every E4M3 value is an fp16 value).
+// `sel` is a constant once the caller's loops are unrolled.
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t w, int sel) {
+  const float f = sel == 0 ? __builtin_amdgcn_cvt_f32_fp8(w, 0)
+                : sel == 1 ? __builtin_amdgcn_cvt_f32_fp8(w, 1)
+                : sel == 2 ? __builtin_amdgcn_cvt_f32_fp8(w, 2)
+                           : __builtin_amdgcn_cvt_f32_fp8(w, 3);
+  return static_cast<_Float16>(f);
+}
+
+__device__ __forceinline__ uint32_t word(const uint4 &v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// ---- operand fragments ------------------------------------------------------------------
+
+// Row-major layout, 32x32x16 MFMA: one lane's share of a 32-row tile for one K step.
+struct Frag {
+  uint4 q[4];       // 4 x 16 bytes of codes: elements [128h + 32q, +32)
+  uint2 s;          // the 8 scale bytes of blocks [8h, 8h + 8) of the step
+};
+
+// codes / scales point at the lane's data for the step; qs = distance between the four
+// 16-byte code pieces.
+__device__ __forceinline__ void load_frag(Frag &f, const uint8_t *codes, const uint8_t *scales, int qs) {
+#pragma unroll
+  for (int q = 0; q < 4; q++) f.q[q] = *reinterpret_cast<const uint4 *>(codes + qs * q);
+  f.s = *reinterpret_cast<const uint2 *>(scales);
+}
+
+// 16x16x32 MFMA: one lane's share of a 16-row tile for one K step.  A lane l = 16g + r holds
+// row r, elements [64g, 64g + 64) of the step in two 32-element pieces; MFMA j = 4q + d
+// (q = 0..1, d = 0..3) takes dword d of piece q, elements [64g + 32q + 8d, +8), whose scale
+// is byte 2q + d/2 of the lane's scale word.  Both operands use this K order (the
+// contraction is order-free and every element carries its own scale).
+struct Frag16 {
+  uint4 q[2];     // code pieces: elements [64g + 32q, +32)
+  uint32_t s;     // scale bytes of blocks [4g, 4g + 4)
+};
+
+__device__ __forceinline__ void load_frag16(Frag16 &f, const uint8_t *codes, const uint8_t *scales, int qs) {
+  f.q[0] = *reinterpret_cast<const uint4 *>(codes);
+  f.q[1] = *reinterpret_cast<const uint4 *>(codes + qs);
+  f.s = *reinterpret_cast<const uint32_t *>(scales);
+}
+
+// Buffer resources (raw, byte-addressed) with hardware range checking: an access at an
+// offset at or past `bytes` returns zeros and reads no memory.  Ranges stay below kOob, so
+// kOob plus any in-range offset is out of range without wrapping.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOob = 0x80000000u;
+static_assert(kMaxPackedBufBytes + 4096 <= kOob, "buffer ranges must stay below the out-of-range offset");
+
+__device__ __forceinline__ BufRsrc make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ void load_frag16_buf(Frag16 &f, BufRsrc rc, uint32_t code_off, uint32_t qs, BufRsrc rs,
+                                                uint32_t scale_off) {
+  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rc, code_off, 0, 0);
+  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rc, code_off + qs, 0, 0);
+  f.q[0] = make_uint4(a.x, a.y, a.z, a.w);
+  f.q[1] = make_uint4(b.x, b.y, b.z, b.w);
+  f.s = __builtin_amdgcn_raw_buffer_load_b32(rs, scale_off, 0, 0);
+}
+
+// ---- epilogue ---------------------------------------------------------------------------
+
+// SwiGLU of one (gate, up) pair of fp32 results already times the global scales: both are
+// rounded to bf16 first, silu(x) = x / (1 + exp(-x)) in binary32 with the hardware exp2 and
+// reciprocal (a few ulp of binary32, far below the bf16 rounding of the result; exp(-x)
+// overflowing to +inf gives silu = -0), the product is rounded to bf16.
+__device__ __forceinline__ uint16_t swiglu_bf16(float gate_acc, float up_acc) {
+  const float gate = round_bf16(gate_acc);
+  const float up = round_bf16(up_acc);
+  const float silu = gate * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gate * -1.4426950408889634f));
+  return f32_to_bf16(silu * up);
+}
+
+// ---- launchers (one per kernel family) -------------------------------------------------
+
+enum Kernel { kLds = 0, kKSplit = 1, kRowMajor = 2 };
+
+// Token tiles (16 rows) per work item of the packed-weight kernels.
+constexpr int kChunkTiles = 3;
+
+void launch_lds(const Params &p, int epi, dim3 grid, hipStream_t stream);
+void launch_ksplit(const Params &p, int epi, int ks, dim3 grid, hipStream_t stream);
+void launch_rowmajor(const Params &p, int epi, int ks, dim3 grid, hipStream_t stream);
+
+}  // namespace gemm
+}  // namespace moe

@@ -1,0 +1,236 @@
+// Grouped NVFP4 GEMM on packed weights with the activation tile shared through LDS -- the
+// kernels for per-expert row counts from a few rows (decode) to hundreds (prefill).
+//
+// A workgroup (four waves) computes one work item: 256 weight rows (each wave owns four
+// 16-row tiles, 64 rows) times the item's chunk of up to MAXT 16-row token tiles, over all
+// of K, with 16x16x32 fp16 MFMA.
+//  * Weights: every weight byte is read once per item, straight into registers, by the one
+//    wave that uses it (packed layout: each load is one contiguous 1 KB or 256 B wave
+//    access), and dequantised there.  Weight fragments alternate between two register
+//    sets: step s + 1 loads while step s computes.
+//  * Activations: the token tiles are the same for the four waves, so each K step's tiles
+//    are dequantised once per workgroup -- wave w turns tiles w, w + 4, ... into fp16 MFMA
+//    operand fragments in LDS (double-buffered, one barrier per step) -- and every wave
+//    reads them back with 16-byte LDS loads (lane-ordered, conflict-free).
+//  * All operand loads are buffer loads through range-checked descriptors.  A load past the
+//    last K step, or for a token tile the chunk does not have, gets an offset beyond the
+//    range: it returns zeros without touching memory.  So every step issues the same loads
+//    unconditionally, and the compiler can count the loads still in flight exactly (a load
+//    behind a branch makes it wait for all of them).
+//  * NM (token tiles of the item) is a template parameter, so the K loop is straight-line
+//    code.
+// Chunks of up to 48 rows (three token tiles), 48 KB of LDS and at most 168 VGPRs, so three
+// workgroups share a CU and overlap one another's loads, dequantisation and MFMAs.  Per step
+// and wave: 264 VALU (weight dequantisation) for 32*NM MFMAs.  At decode sizes the kernel
+// streams weights (HBM-bound); at hundreds of rows per expert it runs the same tile over
+// several chunks, whose repeated weight reads are adjacent items on one XCD and hit its L2.
+// (A 128-row tile with one workgroup per CU measured slower: one wave per SIMD leaves no
+// other wave to issue VALU while the MFMA pipe is busy.)
+#include "gemm_device.hpp"
+
+namespace moe {
+namespace gemm {
+namespace {
+
+template <int MAXT>
+struct LdsShared {
+  uint4 a[2][MAXT][8][64];   // [buffer][token tile][MFMA of step][lane]
+  float wmax[4];
+};
+
+template <int NM, int EPI, int MAXT>
+__device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT> &sh, int b, int e, int row0, int nrows,
+                                         int nt) {
+  constexpr int SPAN = 256;                 // weight rows per workgroup (4 waves x 64)
+  constexpr int TPW = (MAXT + 3) / 4;       // token tiles a wave dequantises per step
+  static_assert(NM <= MAXT, "token tiles exceed the LDS buffer");
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int I = P.N / 2;
+  const int steps = P.K / kKStep;
+
+  int nrow[4];   // first weight row of the wave's four tiles (SwiGLU: gate, gate, up, up)
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    if (EPI == MOE_EPI_SWIGLU) {
+      const int gate = nt * (SPAN / 2) + wv * 32 + (j & 1) * 16;
+      nrow[j] = (j >= 2) ? I + gate : gate;
+    } else {
+      nrow[j] = nt * SPAN + wv * 64 + j * 16;
+    }
+  }
+  const uint32_t expert_bytes = static_cast<uint32_t>(P.N / 16) * steps * kPackBlock;
+  const BufRsrc rb = make_rsrc(P.B + static_cast<int64_t>(e) * expert_bytes, expert_bytes);
+  uint32_t b_code[4], b_scale[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    b_code[j] = static_cast<uint32_t>(nrow[j] / 16) * steps * kPackBlock + lane * 16;
+    b_scale[j] = static_cast<uint32_t>(nrow[j] / 16) * steps * kPackBlock + 2048 + lane * 4;
+  }
+
+  // token tiles wv + 4i this wave dequantises (wave-uniform validity)
+  const uint32_t half_k = P.K / 2, k16 = P.K / 16;
+  const BufRsrc ra_codes = make_rsrc(P.A, static_cast<uint32_t>(P.rows_A * half_k));
+  const BufRsrc ra_scales = make_rsrc(P.A_sf, static_cast<uint32_t>(P.rows_A * k16));
+  bool a_tile[TPW];
+  uint32_t a_code[TPW], a_scale[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; i++) {
+    const int t = wv + 4 * i;
+    a_tile[i] = t < NM;
+    a_code[i] = a_scale[i] = 0;
+    if (a_tile[i]) {
+      const int m = t * 16 + r;
+      int64_t p = row0 + (m < nrows ? m : 0);
+      int64_t src = P.A_rows ? static_cast<int64_t>(P.A_rows[p]) : p;
+      src = src < 0 ? 0 : (src >= P.rows_A ? P.rows_A - 1 : src);
+      a_code[i] = static_cast<uint32_t>(src) * half_k + 32 * g;
+      a_scale[i] = static_cast<uint32_t>(src) * k16 + 4 * g;
+    }
+  }
+  auto load_a = [&](Frag16 (&f)[TPW], int s) {
+#pragma unroll
+    for (int i = 0; i < TPW; i++) {
+      const bool v = a_tile[i] && s < steps;
+      load_frag16_buf(f[i], ra_codes, v ? a_code[i] + s * (kKStep / 2) : kOob, 16, ra_scales,
+                      v ? a_scale[i] + s * (kKStep / 16) : kOob);
+    }
+  };
+  auto store_a = [&](const Frag16 (&f)[TPW], int buf) {
+#pragma unroll
+    for (int i = 0; i < TPW; i++) {
+      if (!a_tile[i]) continue;
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        const half2v sc = e4m3x2_to_f16(f[i].s, q == 1);
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+          const half8 v = dequant8(word(f[i].q[q], d), sc[d >> 1]);
+          sh.a[buf][wv + 4 * i][4 * q + d][lane] = __builtin_bit_cast(uint4, v);
+        }
+      }
+    }
+  };
+  auto load_b = [&](Frag16 (&f)[4], int s) {
+    const uint32_t so = s < steps ? static_cast<uint32_t>(s) * kPackBlock : kOob;
+#pragma unroll
+    for (int j = 0; j < 4; j++) load_frag16_buf(f[j], rb, b_code[j] + so, 1024, rb, b_scale[j] + so);
+  };
+
+  float4v acc[4][NM];
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+#pragma unroll
+    for (int mt = 0; mt < NM; mt++) acc[j][mt] = float4v{};
+
+  // Loads are issued in the same order in the prologue as in every step: the weights of a
+  // step, then the activation tiles of the step after it.
+  Frag16 f0[4], f1[4], ra[TPW], ra0[TPW];
+  load_b(f0, 0);
+  load_a(ra0, 0);
+  load_a(ra, 1);
+  store_a(ra0, 0);
+  __syncthreads();
+
+  auto step = [&](const Frag16 (&fb)[4], Frag16 (&fl)[4], int s) {
+    const int buf = s & 1;
+    load_b(fl, s + 1);
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      half2v bsc[4];   // scales of blocks 2q, 2q + 1 of each weight tile
+#pragma unroll
+      for (int j = 0; j < 4; j++) bsc[j] = e4m3x2_to_f16(fb[j].s, q == 1);
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        half8 af[NM];
+#pragma unroll
+        for (int mt = 0; mt < NM; mt++) af[mt] = __builtin_bit_cast(half8, sh.a[buf][mt][4 * q + d][lane]);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const half8 bf = dequant8(word(fb[j].q[q], d), bsc[j][d >> 1]);
+#pragma unroll
+          for (int mt = 0; mt < NM; mt++)
+            acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[mt], acc[j][mt], 0, 0, 0);
+        }
+      }
+    }
+    if (s + 1 < steps) store_a(ra, buf ^ 1);   // activation tiles of step s + 1
+    load_a(ra, s + 2);
+    __syncthreads();
+  };
+  int s = 0;
+  for (; s + 2 <= steps; s += 2) {
+    step(f0, f1, s);
+    step(f1, f0, s + 1);
+  }
+  if (s < steps) step(f0, f1, s);
+
+  // epilogue: 16x16 D lane layout -- weight row 4g + i, token row r of the tile
+  const float gscale = (*P.A_gs) * P.B_gs[e];
+  float amax = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < NM; mt++) {
+    const int m = mt * 16 + r;
+    if (m < nrows) {
+      const int64_t p = row0 + m;
+      if (EPI == MOE_EPI_NONE) {
+        uint16_t *drow = static_cast<uint16_t *>(P.D) + p * P.N;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const uint32_t lo = f32_to_bf16(acc[j][mt][0] * gscale) |
+                              (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][1] * gscale)) << 16);
+          const uint32_t hi = f32_to_bf16(acc[j][mt][2] * gscale) |
+                              (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][3] * gscale)) << 16);
+          *reinterpret_cast<uint2 *>(drow + nrow[j] + 4 * g) = make_uint2(lo, hi);
+        }
+      } else {
+        uint16_t *drow = static_cast<uint16_t *>(P.D) + p * I;
+#pragma unroll
+        for (int jp = 0; jp < 2; jp++) {
+          uint16_t o[4];
+#pragma unroll
+          for (int c = 0; c < 4; c++) {
+            o[c] = swiglu_bf16(acc[jp][mt][c] * gscale, acc[2 + jp][mt][c] * gscale);
+            amax = fmaxf(amax, fabsf(bf16_to_f32(o[c])));
+          }
+          *reinterpret_cast<uint2 *>(drow + nrow[jp] + 4 * g) =
+              make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+        }
+      }
+    }
+  }
+  if (EPI == MOE_EPI_SWIGLU) {
+    amax = wave_max(amax);
+    if (lane == 0) sh.wmax[wv] = amax;
+    __syncthreads();
+    if (threadIdx.x == 0) P.amax_out[b] = fmaxf(fmaxf(sh.wmax[0], sh.wmax[1]), fmaxf(sh.wmax[2], sh.wmax[3]));
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 3) void gemm_lds_kernel(Params P) {
+  __shared__ LdsShared<kChunkTiles> sh;
+  const int b = blockIdx.x;
+  int4 item;
+  if (!item_for_block(P, b, item)) {
+    if (EPI == MOE_EPI_SWIGLU && threadIdx.x == 0) P.amax_out[b] = 0.f;
+    return;
+  }
+  const int nm = (item.z + 15) / 16;   // workgroup-uniform
+  if (nm <= 1) lds_body<1, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
+  else if (nm == 2) lds_body<2, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
+  else lds_body<3, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
+}
+
+}  // namespace
+
+void launch_lds(const Params &p, int epi, dim3 grid, hipStream_t stream) {
+  const dim3 block(256);
+  if (epi == MOE_EPI_SWIGLU) hipLaunchKernelGGL(gemm_lds_kernel<MOE_EPI_SWIGLU>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(gemm_lds_kernel<MOE_EPI_NONE>, grid, block, 0, stream, p);
+}
+
+}  // namespace gemm
+}  // namespace moe

@@ -138,7 +138,8 @@ moe_status moe_quantize_nvfp4(const void *x, int x_dtype, int64_t rows, int64_t 
  *   MOE_EPI_NONE    D bf16 [R, N]: D[p, n] = bf16(y[p, n]).
  *   MOE_EPI_SWIGLU  N = 2I; columns [0, I) are gate, [I, 2I) are up;
  *                   D bf16 [R, I]: D[p, i] = bf16(silu(bf16(y[p, i])) * bf16(y[p, I+i]))
- *                   with silu(x) = x / (1 + exp(-x)) in binary32, and
+ *                   with silu(x) = x / (1 + exp(-x)) in binary32 (hardware exp2 and
+ *                   reciprocal: a few ulp of binary32), and
  *                   amax_out[moe_grouped_gemm_nvfp4_amax_slots(args)] f32 receives
  *                   partial maxima of |D| (their maximum is max|D|; unused slots 0),
  *                   for moe_quantize_nvfp4(..., amax_in = amax_out, ...).

@@ -211,6 +211,10 @@ def _run_gemm_none(A, Bs, off, A_rows, R, label, packed=False):
     ([0, 0, 0], 256, 256, False),                         # no rows at all
     ([300], 256, 768, True),                              # one big group: several row chunks
     ([33] * 250 + [0, 64, 5] + [20] * 10, 256, 1024, True),  # enough groups for 4 tiles per wave
+    # hundreds of rows per expert (several row chunks each, every remainder 1..47 rows) and,
+    # in the second case, an odd number of 256-wide K steps
+    ([0, 1, 96, 127, 128, 129, 300, 513], 512, 512, True),
+    ([100, 200, 57, 0], 768, 256, True),
 ])
 def test_gemm_none_shapes(sizes, K, N, gather, packed):
     A, Bs, off, A_rows, R = _gemm_case(sizes, K, N, gather, seed=sum(sizes) + K + N)
@@ -283,7 +287,8 @@ def _run_gemm_swiglu(A, Bs, off, A_rows, R, label, rows=None, packed=False):
 
 @pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
 @pytest.mark.parametrize("sizes,K,I", [([8, 6, 9, 9], 256, 256), ([0, 17, 33, 64, 65, 1], 512, 384),
-                                       ([40] * 256 + [3, 0, 64], 256, 512)])
+                                       ([40] * 256 + [3, 0, 64], 256, 512),
+                                       ([0, 130, 255, 97], 768, 256)])   # several chunks, odd K steps
 def test_gemm_swiglu_shapes(sizes, K, I, packed):
     A, Bs, off, A_rows, R = _gemm_case(sizes, K, 2 * I, True, seed=7 + K + I)
     _run_gemm_swiglu(A, Bs, off, A_rows, R, f"sizes={sizes}", packed=packed)
