@@ -67,6 +67,7 @@ struct GemmPlan {
   int n_tiles;       // N / n_tile
   int64_t max_items; // upper bound on (expert, row chunk, n tile) work items
   int64_t grid;      // workgroups launched (max_items rounded up to the XCD count)
+  bool inline_schedule;  // waves derive their items from the offsets (no schedule kernel)
   size_t ws_bytes;
 };
 GemmPlan plan_gemm(const moe_gemm_args &a);

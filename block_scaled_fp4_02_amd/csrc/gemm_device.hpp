@@ -30,21 +30,104 @@ struct Params {
   int E, N, K;
   void *D;
   float *amax_out;
-  const int4 *items;   // (expert, first row, rows, n tile), from the schedule kernel
-  const int *count;    // number of valid items
+  // Work items (expert, first row, rows, n tile), ordered expert-major, then n tile, then
+  // row chunk.  With items == nullptr every wave derives its own from the offsets.
+  const int4 *items;   // from the schedule kernel, or nullptr
+  const int *count;    // number of valid items (with items)
+  const int32_t *offsets;
+  int64_t R;
+  int chunk_rows, n_tiles;
 };
+
+// Largest expert count for which waves derive their work item from the offsets themselves
+// (one wave-wide pass each for the count and the item); above it, repeating the passes in
+// thousands of workgroups costs more than one schedule kernel that writes the item list.
+constexpr int kMaxInlineScheduleExperts = 64;
+
+// Rows of expert e (offsets clamped to [0, R] and made monotone) and its first row.
+__device__ __forceinline__ int expert_rows(const Params &P, int e, int64_t &lo) {
+  lo = P.offsets[e];
+  lo = lo < 0 ? 0 : (lo > P.R ? P.R : lo);
+  int64_t hi = P.offsets[e + 1];
+  hi = hi < lo ? lo : (hi > P.R ? P.R : hi);
+  return static_cast<int>(hi - lo);
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
 
 // Work item of workgroup b, or false if it has none.  Workgroup b runs on XCD b % 8, so
 // the items are dealt to XCDs in contiguous ranges: neighbouring items (the n tiles and row
-// chunks of one expert) share that XCD's L2.
+// chunks of one expert) share that XCD's L2.  The result is wave-uniform.
 __device__ __forceinline__ bool item_for_block(const Params &P, int b, int4 &item) {
-  const int count = *P.count;
+  const int lane = threadIdx.x & 63;
+  const int cr = P.chunk_rows;
+  int count;
+  if (P.items) {
+    count = *P.count;
+  } else {
+    count = 0;
+    for (int base = 0; base < P.E; base += kWave) {
+      const int e = base + lane;
+      int mine = 0;
+      if (e < P.E) {
+        int64_t lo;
+        mine = (expert_rows(P, e, lo) + cr - 1) / cr * P.n_tiles;
+      }
+      count += wave_sum(mine);
+    }
+    count = __builtin_amdgcn_readfirstlane(count);   // uniform: keep it (and w) in SGPRs
+  }
   const int per_xcd = (count + kXcds - 1) / kXcds;
   const int jx = b / kXcds;
   const int w = (b % kXcds) * per_xcd + jx;
   if (jx >= per_xcd || w >= count) return false;
-  item = P.items[w];
-  return true;
+  if (P.items) {
+    item = P.items[w];
+    return true;
+  }
+  int carry = 0;   // items of the experts before this group of 64
+  for (int base = 0; base < P.E; base += kWave) {
+    const int e = base + lane;
+    int64_t lo = 0;
+    int rows = 0, chunks = 0;
+    if (e < P.E) {
+      rows = expert_rows(P, e, lo);
+      chunks = (rows + cr - 1) / cr;
+    }
+    const int mine = chunks * P.n_tiles;
+    const int incl = wave_inclusive_scan(mine);
+    const int local = w - carry - (incl - mine);   // index of w among expert e's items
+    const uint64_t owner = __ballot(mine > 0 && local >= 0 && local < mine);
+    if (owner) {
+      // the owner lane's values, read as scalars so that everything the kernel derives
+      // from the item stays in SGPRs
+      const int src = __builtin_ctzll(owner);
+      const int c_src = __builtin_amdgcn_readlane(chunks, src);
+      const int l_src = __builtin_amdgcn_readlane(local, src);
+      const int rows_src = __builtin_amdgcn_readlane(rows, src);
+      const int lo_src = __builtin_amdgcn_readlane(static_cast<int>(lo), src);
+      const int nt = l_src / c_src, c = l_src % c_src;
+      const int nr = rows_src - c * cr;
+      item = make_int4(base + src, lo_src + c * cr, nr < cr ? nr : cr, nt);
+      return true;
+    }
+    carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+  }
+  return false;   // not reached: w < count
 }
 
 // ---- dequantisation ------------------------------------------------------------------
@@ -155,6 +238,8 @@ constexpr int kChunkTiles = 3;
 
 void launch_lds(const Params &p, int epi, dim3 grid, hipStream_t stream);
 void launch_ksplit(const Params &p, int epi, int ks, dim3 grid, hipStream_t stream);
+int ksplit_chunk_rows();      // rows per work item of the K-split kernel
+int ksplit_waves(int ks);     // waves per workgroup of the K-split kernel
 void launch_rowmajor(const Params &p, int epi, int ks, dim3 grid, hipStream_t stream);
 
 }  // namespace gemm

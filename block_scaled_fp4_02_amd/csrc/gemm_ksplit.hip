@@ -1,19 +1,34 @@
-// Grouped NVFP4 GEMM on packed weights for few groups (e.g. 8 experts x 32 rows): the four
-// waves of a workgroup split K (2 or 4 ways) so that a grid of few (expert, n tile) items
-// still has enough waves, and add their partial tiles in LDS in a fixed order
-// (deterministic).  Each wave dequantises its own weight and activation fragments into
-// registers (16x16x32 fp16 MFMA, fragment K order as in gemm_device.hpp); a workgroup covers
-// (4 / KS) * 64 weight rows.
+// Grouped NVFP4 GEMM on packed weights for few work items (e.g. one 8-expert grouped GEMM of
+// 32 rows each): the waves of a workgroup split K (KS = 2, 4 or 8 ways) so that a grid of
+// few (expert, n tile) items still puts two waves on every SIMD, and add their partial tiles
+// in LDS in a fixed order (deterministic).
+//
+// A workgroup has max(4, KS) waves: NG = waves / KS groups of 64 weight rows, each split
+// over KS waves that take consecutive K ranges.  Chunks hold up to 32 rows (two 16-row
+// token tiles).  Each wave dequantises its own weight and activation fragments into
+// registers (16x16x32 fp16 MFMA, fragment K order as in gemm_device.hpp).  Weight and
+// activation fragments rotate through three register sets, so the loads of step s + 2 are
+// in flight while step s computes -- with few steps per wave (e.g. 3 at K = 6144, KS = 8)
+// every load of the wave is issued before its first MFMA.  All loads are unconditional
+// range-checked buffer loads (past the wave's K range they return zeros and read nothing),
+// so the compiler counts the loads in flight exactly.
 #include "gemm_device.hpp"
 
 namespace moe {
 namespace gemm {
 namespace {
 
+constexpr int kSplitTiles = 2;                       // token tiles per chunk
+constexpr int kSplitTile = 4 * kSplitTiles * 4 * 64;  // floats of one wave's partial tile
+
+template <int KS>
+constexpr int split_waves() { return KS < 4 ? 4 : KS; }
+
 template <int NM, int KS, int EPI>
 __device__ __forceinline__ void ks_body(const Params &P, float *red, float *wmax, int b, int e,
                                         int row0, int nrows, int nt) {
-  constexpr int NG = 4 / KS;
+  constexpr int WAVES = split_waves<KS>();
+  constexpr int NG = WAVES / KS;
   constexpr int SPAN = NG * 64;   // weight rows per workgroup
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -23,6 +38,8 @@ __device__ __forceinline__ void ks_body(const Params &P, float *red, float *wmax
   const int g = lane >> 4;        // K group of the lane
   const int I = P.N / 2;
   const int steps = P.K / kKStep;
+  const int iters = steps / KS;
+  const int s_begin = kq * iters;
 
   // first weight row of the wave's four 16-row tiles (SwiGLU: gate, gate, up, up)
   int nrow[4];
@@ -35,24 +52,42 @@ __device__ __forceinline__ void ks_body(const Params &P, float *red, float *wmax
       nrow[j] = nt * SPAN + ng * 64 + j * 16;
     }
   }
-  // weight tiles: wave-uniform base pointers, per-lane 32-bit offsets
-  const uint8_t *bbase[4];
+  const uint32_t expert_bytes = static_cast<uint32_t>(P.N / 16) * steps * kPackBlock;
+  const BufRsrc rb = make_rsrc(P.B + static_cast<int64_t>(e) * expert_bytes, expert_bytes);
+  uint32_t b_code[4], b_scale[4];
 #pragma unroll
-  for (int j = 0; j < 4; j++)
-    bbase[j] = P.B + (static_cast<int64_t>(e) * P.N + nrow[j]) / 16 * steps * kPackBlock;
-  const uint32_t b_code_off = lane * 16, b_scale_off = 2048 + lane * 4;
-  // token rows of the NM 16-row tiles of the chunk: 32-bit offsets into A
-  // (rows_A * K / 2 < 2^32 is checked on the host)
+  for (int j = 0; j < 4; j++) {
+    const uint32_t t = static_cast<uint32_t>(nrow[j] / 16) * steps * kPackBlock;
+    b_code[j] = t + lane * 16;
+    b_scale[j] = t + 2048 + lane * 4;
+  }
   const uint32_t half_k = P.K / 2, k16 = P.K / 16;
-  uint32_t aoff[NM];
+  const BufRsrc ra_codes = make_rsrc(P.A, static_cast<uint32_t>(P.rows_A * half_k));
+  const BufRsrc ra_scales = make_rsrc(P.A_sf, static_cast<uint32_t>(P.rows_A * k16));
+  uint32_t a_code[NM], a_scale[NM];
 #pragma unroll
   for (int mt = 0; mt < NM; mt++) {
     const int m = mt * 16 + r;
     int64_t p = row0 + (m < nrows ? m : 0);
     int64_t src = P.A_rows ? static_cast<int64_t>(P.A_rows[p]) : p;
     src = src < 0 ? 0 : (src >= P.rows_A ? P.rows_A - 1 : src);
-    aoff[mt] = static_cast<uint32_t>(src);
+    a_code[mt] = static_cast<uint32_t>(src) * half_k + 32 * g;
+    a_scale[mt] = static_cast<uint32_t>(src) * k16 + 4 * g;
   }
+  // it: step index within the wave's K range
+  auto load_b = [&](Frag16 (&f)[4], int it) {
+    const uint32_t so = it < iters ? static_cast<uint32_t>(s_begin + it) * kPackBlock : kOob;
+#pragma unroll
+    for (int j = 0; j < 4; j++) load_frag16_buf(f[j], rb, b_code[j] + so, 1024, rb, b_scale[j] + so);
+  };
+  auto load_a = [&](Frag16 (&f)[NM], int it) {
+    const bool v = it < iters;
+    const uint32_t s = static_cast<uint32_t>(s_begin + it);
+#pragma unroll
+    for (int mt = 0; mt < NM; mt++)
+      load_frag16_buf(f[mt], ra_codes, v ? a_code[mt] + s * (kKStep / 2) : kOob, 16, ra_scales,
+                      v ? a_scale[mt] + s * (kKStep / 16) : kOob);
+  };
 
   float4v acc[4][NM];
 #pragma unroll
@@ -60,29 +95,14 @@ __device__ __forceinline__ void ks_body(const Params &P, float *red, float *wmax
 #pragma unroll
     for (int mt = 0; mt < NM; mt++) acc[j][mt] = float4v{};
 
-  const int s_begin = kq * (steps / KS);
-  const int iters = steps / KS;
-  Frag16 fb[4], fa[NM], nb[4], na[NM];
-  auto load_b = [&](Frag16 (&f)[4], int s) {
-    const uint32_t so = static_cast<uint32_t>(s) * kPackBlock;
-#pragma unroll
-    for (int j = 0; j < 4; j++) load_frag16(f[j], bbase[j] + (so + b_code_off), bbase[j] + (so + b_scale_off), 1024);
-  };
-  auto load_a = [&](Frag16 (&f)[NM], int s) {
-#pragma unroll
-    for (int mt = 0; mt < NM; mt++)
-        load_frag16(f[mt], P.A + (aoff[mt] * half_k + 32 * g + s * (kKStep / 2)),
-                    P.A_sf + (aoff[mt] * k16 + 4 * g + s * (kKStep / 16)), 16);
-  };
-  load_a(fa, s_begin);
-  load_b(fb, s_begin);
-
-  for (int it = 0; it < iters; it++) {
-    const bool more = it + 1 < iters;
-    if (more) {
-      load_a(na, s_begin + it + 1);
-      load_b(nb, s_begin + it + 1);
-    }
+  Frag16 b0[4], b1[4], b2[4], a0[NM], a1[NM], a2[NM];
+  load_b(b0, 0);
+  load_a(a0, 0);
+  load_b(b1, 1);
+  load_a(a1, 1);
+  auto step = [&](const Frag16 (&fb)[4], const Frag16 (&fa)[NM], Frag16 (&bl)[4], Frag16 (&al)[NM], int it) {
+    load_b(bl, it + 2);
+    load_a(al, it + 2);
 #pragma unroll
     for (int q = 0; q < 2; q++) {
       half2v bsc[4], asc[NM];
@@ -94,8 +114,7 @@ __device__ __forceinline__ void ks_body(const Params &P, float *red, float *wmax
       for (int d = 0; d < 4; d++) {
         half8 af[NM];
 #pragma unroll
-        for (int mt = 0; mt < NM; mt++)
-          af[mt] = dequant8(word(fa[mt].q[q], d), asc[mt][d >> 1]);
+        for (int mt = 0; mt < NM; mt++) af[mt] = dequant8(word(fa[mt].q[q], d), asc[mt][d >> 1]);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           const half8 bf = dequant8(word(fb[j].q[q], d), bsc[j][d >> 1]);
@@ -105,36 +124,37 @@ __device__ __forceinline__ void ks_body(const Params &P, float *red, float *wmax
         }
       }
     }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < 4; j++) fb[j] = nb[j];
-#pragma unroll
-      for (int mt = 0; mt < NM; mt++) fa[mt] = na[mt];
-    }
+  };
+  int it = 0;
+  for (; it + 3 <= iters; it += 3) {
+    step(b0, a0, b2, a2, it);
+    step(b1, a1, b0, a0, it + 1);
+    step(b2, a2, b1, a1, it + 2);
   }
+  if (it < iters) step(b0, a0, b2, a2, it);
+  if (it + 1 < iters) step(b1, a1, b0, a0, it + 1);
 
-  if constexpr (KS > 1) {
-    constexpr int TILE = 4 * kChunkTiles * 4 * 64;
-    float *mine = red + ((kq - 1) * NG + ng) * TILE;
-    if (kq > 0) {
+  // K parts 1..KS-1 leave their partial tiles in LDS; part 0 adds them in order 1, 2, ...
+  if (kq > 0) {
+    float *mine = red + ((kq - 1) * NG + ng) * kSplitTile;
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int mt = 0; mt < NM; mt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) mine[((j * kSplitTiles + mt) * 4 + i) * 64 + lane] = acc[j][mt][i];
+  }
+  __syncthreads();
+  if (kq == 0) {
+#pragma unroll 1
+    for (int o = 1; o < KS; o++) {   // rolled: one partial tile's loads in flight at a time
+      const float *src = red + ((o - 1) * NG + ng) * kSplitTile;
 #pragma unroll
       for (int j = 0; j < 4; j++)
 #pragma unroll
         for (int mt = 0; mt < NM; mt++)
 #pragma unroll
-          for (int i = 0; i < 4; i++) mine[((j * kChunkTiles + mt) * 4 + i) * 64 + lane] = acc[j][mt][i];
-    }
-    __syncthreads();
-    if (kq == 0) {
-      for (int o = 1; o < KS; o++) {
-        const float *src = red + ((o - 1) * NG + ng) * TILE;
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-#pragma unroll
-          for (int mt = 0; mt < NM; mt++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) acc[j][mt][i] += src[((j * kChunkTiles + mt) * 4 + i) * 64 + lane];
-      }
+          for (int i = 0; i < 4; i++) acc[j][mt][i] += src[((j * kSplitTiles + mt) * 4 + i) * 64 + lane];
     }
   }
 
@@ -178,38 +198,45 @@ __device__ __forceinline__ void ks_body(const Params &P, float *red, float *wmax
     amax = wave_max(amax);
     if (lane == 0) wmax[wv] = amax;
     __syncthreads();
-    if (threadIdx.x == 0) P.amax_out[b] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    if (threadIdx.x == 0) {
+      float m = wmax[0];
+      for (int w = 1; w < WAVES; w++) m = fmaxf(m, wmax[w]);
+      P.amax_out[b] = m;
+    }
   }
 }
 
+// Two waves per SIMD: 4-wave workgroups two per CU, 8-wave workgroups one per CU.
 template <int KS, int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_ksplit_kernel(Params P) {
-  constexpr int TILE = 4 * kChunkTiles * 4 * 64;
-  __shared__ float red[KS > 1 ? (KS - 1) * (4 / KS) * TILE : 1];
-  __shared__ float wmax[4];
+__global__ __launch_bounds__(64 * split_waves<KS>(), 8 / split_waves<KS>()) void gemm_ksplit_kernel(Params P) {
+  constexpr int WAVES = split_waves<KS>();
+  __shared__ float red[(KS - 1) * (WAVES / KS) * kSplitTile];
+  __shared__ float wmax[WAVES];
   const int b = blockIdx.x;
   int4 item;
   if (!item_for_block(P, b, item)) {
     if (EPI == MOE_EPI_SWIGLU && threadIdx.x == 0) P.amax_out[b] = 0.f;
     return;
   }
-  const int nm = (item.z + 15) / 16;   // workgroup-uniform
-  if (nm <= 1) ks_body<1, KS, EPI>(P, red, wmax, b, item.x, item.y, item.z, item.w);
-  else if (nm == 2) ks_body<2, KS, EPI>(P, red, wmax, b, item.x, item.y, item.z, item.w);
-  else ks_body<3, KS, EPI>(P, red, wmax, b, item.x, item.y, item.z, item.w);
+  if (item.z <= 16) ks_body<1, KS, EPI>(P, red, wmax, b, item.x, item.y, item.z, item.w);
+  else ks_body<2, KS, EPI>(P, red, wmax, b, item.x, item.y, item.z, item.w);
+}
+
+template <int EPI>
+void launch_epi(const Params &p, int ks, dim3 grid, hipStream_t stream) {
+  if (ks == 2) hipLaunchKernelGGL((gemm_ksplit_kernel<2, EPI>), grid, dim3(64 * split_waves<2>()), 0, stream, p);
+  else if (ks == 4) hipLaunchKernelGGL((gemm_ksplit_kernel<4, EPI>), grid, dim3(64 * split_waves<4>()), 0, stream, p);
+  else hipLaunchKernelGGL((gemm_ksplit_kernel<8, EPI>), grid, dim3(64 * split_waves<8>()), 0, stream, p);
 }
 
 }  // namespace
 
+int ksplit_chunk_rows() { return kSplitTiles * 16; }
+int ksplit_waves(int ks) { return ks < 4 ? 4 : ks; }
+
 void launch_ksplit(const Params &p, int epi, int ks, dim3 grid, hipStream_t stream) {
-  const dim3 block(256);
-  if (epi == MOE_EPI_SWIGLU) {
-    if (ks == 2) hipLaunchKernelGGL((gemm_ksplit_kernel<2, MOE_EPI_SWIGLU>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((gemm_ksplit_kernel<4, MOE_EPI_SWIGLU>), grid, block, 0, stream, p);
-  } else {
-    if (ks == 2) hipLaunchKernelGGL((gemm_ksplit_kernel<2, MOE_EPI_NONE>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((gemm_ksplit_kernel<4, MOE_EPI_NONE>), grid, block, 0, stream, p);
-  }
+  if (epi == MOE_EPI_SWIGLU) launch_epi<MOE_EPI_SWIGLU>(p, ks, grid, stream);
+  else launch_epi<MOE_EPI_NONE>(p, ks, grid, stream);
 }
 
 }  // namespace gemm

@@ -10,13 +10,16 @@
 // NONE"), plus a SwiGLU epilogue for the gate/up projection.
 //
 // Design (not the pages' SM120 tiles; this is for gfx950):
-//  * Work list: a one-workgroup schedule kernel turns expert_offsets into items (expert,
-//    row chunk, n tile), ordered expert-major, then n tile, then chunk.  The grid is the
-//    host-side upper bound on the item count; items past the device-side count exit.
+//  * Work list: items (expert, row chunk, n tile), ordered expert-major, then n tile, then
+//    chunk.  Up to 64 experts every wave derives its own item from expert_offsets (a
+//    wave-wide sum and scan, no extra launch); above that a one-workgroup schedule kernel
+//    writes the list first.  The grid is the host-side upper bound on the
+//    item count; items past the device-side count exit.
 //  * Per-shape plan (the counterpart of the pages' tile table, chosen from host-known sizes
 //    only, so a supported launch cannot fail on its configuration):
 //      packed weights, enough items for the chip   -> LDS kernel, 48-row chunks
-//      packed weights, few items (e.g. 8 groups)   -> K split across a workgroup's waves
+//      packed weights, few items (e.g. 8 groups)   -> K split 2/4/8 ways across a
+//                                                     workgroup's waves, 32-row chunks
 //      row-major weights                           -> 32x32 MFMA kernel, 64-row chunks
 //    Kernel details are in gemm_lds.hip, gemm_ksplit.hip and gemm_rowmajor.hip.
 #include "gemm_device.hpp"
@@ -113,39 +116,64 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ B
 
 using namespace gemm;
 
+// Work items and waves for `chunk` rows per item: every expert has at least one chunk in
+// the estimate, an empty one none (the grid bound counts one extra chunk per expert).
+static int64_t chunk_estimate(const moe_gemm_args &a, int chunk) {
+  return std::max<int64_t>(a.E, (a.R + chunk - 1) / chunk);
+}
+
 GemmPlan plan_gemm(const moe_gemm_args &a) {
   GemmPlan p{};
-  const bool packed = a.B_layout == MOE_LAYOUT_PACKED;
-  p.kernel = packed ? kLds : kRowMajor;
-  p.chunk_rows = packed ? kChunkTiles * 16 : 64;
-  const int chunk = p.chunk_rows;
-  const int64_t chunk_bound = (a.R + chunk - 1) / chunk + a.E;
-  const int64_t chunk_est = std::max<int64_t>(a.E, (a.R + chunk - 1) / chunk);
-  // A workgroup covers 256 weight rows (four waves x 64); for few items the waves split K
-  // (2 or 4 ways) so that there are at least ~2 workgroups per CU.
-  p.ks = 1;
-  for (int cand = 1; cand <= 4; cand *= 2) {
-    if (a.K % (kKStep * cand) != 0) break;
-    p.ks = cand;
-    if (chunk_est * (a.N / (256 / cand)) >= 2 * 256) break;
+  constexpr int64_t kFullChip = 2 * 4 * 256;   // two waves on every SIMD of the 256 CUs
+  if (a.B_layout == MOE_LAYOUT_PACKED) {
+    p.kernel = kLds;
+    p.chunk_rows = kChunkTiles * 16;
+    p.ks = 1;
+    p.n_tile = 256;
+    if (chunk_estimate(a, p.chunk_rows) * (a.N / 256) * 4 < kFullChip) {
+      // few items: split K across the waves of a workgroup (2, 4 or 8 ways)
+      const int chunk = ksplit_chunk_rows();
+      for (int cand = 2; cand <= 8; cand *= 2) {
+        if (a.K % (kKStep * cand) != 0) break;
+        p.kernel = kKSplit;
+        p.chunk_rows = chunk;
+        p.ks = cand;
+        p.n_tile = 64 * (ksplit_waves(cand) / cand);
+        if (chunk_estimate(a, chunk) * (a.N / p.n_tile) * ksplit_waves(cand) >= kFullChip) break;
+      }
+    }
+  } else {
+    // row-major weights: four waves of two 32-row tiles, K split 1, 2 or 4 ways
+    p.kernel = kRowMajor;
+    p.chunk_rows = 64;
+    p.ks = 1;
+    for (int cand = 1; cand <= 4; cand *= 2) {
+      if (a.K % (kKStep * cand) != 0) break;
+      p.ks = cand;
+      if (chunk_estimate(a, p.chunk_rows) * (a.N / (256 / cand)) >= 2 * 256) break;
+    }
+    p.n_tile = 256 / p.ks;
   }
-  if (packed && p.ks > 1) p.kernel = kKSplit;
-  p.n_tile = 256 / p.ks;
   p.n_tiles = a.N / p.n_tile;
+  const int64_t chunk_bound = (a.R + p.chunk_rows - 1) / p.chunk_rows + a.E;
   p.max_items = static_cast<int64_t>(p.n_tiles) * chunk_bound;
   p.grid = (p.max_items + kXcds - 1) / kXcds * kXcds;
-  p.ws_bytes = 16 + static_cast<size_t>(p.max_items) * sizeof(int4);
+  p.inline_schedule = a.E <= kMaxInlineScheduleExperts;
+  p.ws_bytes = p.inline_schedule ? 16 : 16 + static_cast<size_t>(p.max_items) * sizeof(int4);
   return p;
 }
 
 hipError_t launch_grouped_gemm(const moe_gemm_args &a, const GemmPlan &plan, void *ws,
                                hipStream_t stream) {
   int *count = static_cast<int *>(ws);
-  int4 *items = reinterpret_cast<int4 *>(static_cast<char *>(ws) + 16);
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, stream, a.expert_offsets, a.E, a.R,
-                     plan.chunk_rows, plan.n_tiles, plan.max_items, items, count);
+  int4 *items = nullptr;
+  if (!plan.inline_schedule) {
+    items = reinterpret_cast<int4 *>(static_cast<char *>(ws) + 16);
+    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, stream, a.expert_offsets, a.E, a.R,
+                       plan.chunk_rows, plan.n_tiles, plan.max_items, items, count);
+  }
   const Params p{a.A, a.A_sf, a.A_gs, a.A_rows, a.rows_A, a.B, a.B_sf, a.B_gs, a.E, a.N, a.K,
-                 a.D, a.amax_out, items, count};
+                 a.D, a.amax_out, items, count, a.expert_offsets, a.R, plan.chunk_rows, plan.n_tiles};
   const dim3 grid(static_cast<uint32_t>(plan.grid));
   switch (plan.kernel) {
     case kLds: launch_lds(p, a.epilogue, grid, stream); break;

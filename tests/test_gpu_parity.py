@@ -208,6 +208,7 @@ def _run_gemm_none(A, Bs, off, A_rows, R, label, packed=False):
     ([0, 1, 31, 32, 33, 64, 65, 130, 0], 512, 256, True),  # ragged groups, empty groups, tails
     ([40, 0, 3], 1536, 256, False),                       # K split 2 ways inside a workgroup
     ([7, 25], 1024, 512, False),                          # K split 4 ways
+    ([45, 3], 2048, 256, True),                           # K split 8 ways, 32 + 13 row chunks
     ([0, 0, 0], 256, 256, False),                         # no rows at all
     ([300], 256, 768, True),                              # one big group: several row chunks
     ([33] * 250 + [0, 64, 5] + [20] * 10, 256, 1024, True),  # enough groups for 4 tiles per wave
@@ -288,7 +289,8 @@ def _run_gemm_swiglu(A, Bs, off, A_rows, R, label, rows=None, packed=False):
 @pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
 @pytest.mark.parametrize("sizes,K,I", [([8, 6, 9, 9], 256, 256), ([0, 17, 33, 64, 65, 1], 512, 384),
                                        ([40] * 256 + [3, 0, 64], 256, 512),
-                                       ([0, 130, 255, 97], 768, 256)])   # several chunks, odd K steps
+                                       ([0, 130, 255, 97], 768, 256),    # several chunks, odd K steps
+                                       ([20, 32], 2048, 256)])           # K split 8 ways
 def test_gemm_swiglu_shapes(sizes, K, I, packed):
     A, Bs, off, A_rows, R = _gemm_case(sizes, K, 2 * I, True, seed=7 + K + I)
     _run_gemm_swiglu(A, Bs, off, A_rows, R, f"sizes={sizes}", packed=packed)
