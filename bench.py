@@ -43,6 +43,32 @@ def parse():
     return ap.parse_args()
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "layer_decode_t1024_e256_k8_hbm_traffic.md")
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy of known size), or None when the summary is missing or the
+    kernel sources changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    blob = json.loads(m.group(1))
+    h = hashlib.sha256()
+    for p in blob["kernel_sources"]:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != blob["kernel_sources_sha256"] or kernel not in blob["per_launch"]:
+        return None
+    return blob["per_launch"][kernel]["bytes"]
+
+
 def copy_calibration(mib: int):
     import torch
     n = mib << 20
@@ -240,9 +266,10 @@ def main():
                                                                            int(sizes.max())],
                    "operands": "NVFP4 (e2m1, e4m3 scale per 16, f32 global) dequantised exactly to fp16 MFMA, fp32 accumulate",
                    "weights_layout": "packed"},
-        "roofline": {"kernel": "grouped_gemm_kernel (gate/up + SwiGLU)", "bound": "hbm",
+        "roofline": {"kernel": "gemm_lds_kernel<1> (gate/up + SwiGLU)", "bound": "hbm",
                      "achieved": round(g1_alg_bytes / g1_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(g1_alg_bytes / g1_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(g1_alg_bytes / g1_s / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("moe::gemm::gemm_lds_kernel<1>") if L is synth.LAYER_DECODE else None,
                      "alg_bytes_per_launch": int(g1_alg_bytes), "avg_launch_us": round(stage_us["gemm1"], 2)},
         "gemm_tflops": round((gemm1_flops + gemm2_flops) / (g1_s + g2_s) / 1e12, 2),
         "weight_hbm_GBps": round(weight_gbps, 1),
