@@ -7,8 +7,9 @@ library's gfx950 kernels; there is no fallback.  If the library has not been bui
 import of any entry point fails loudly.
 
 Functions with the C names take caller-allocated tensors exactly like the C calls.  The
-``*_alloc`` helpers and :func:`moe_layer_forward` allocate outputs and workspaces with
-torch and sequence the calls of one MoE layer.
+``*_alloc`` helpers allocate outputs and workspaces with torch; :func:`pack_weights` turns
+an NVFP4 weight tensor into the packed layout once; :class:`MoELayerPlan` pre-allocates one
+MoE layer's buffers and sequences its six calls.
 """
 from __future__ import annotations
 
