@@ -25,8 +25,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE grouped-GEMM TFLOPS + weight HBM GB/s (% roofline) at ~32 tok/expert"
 HBM_PEAK_GBPS = 8000.0
+F16_PEAK_TFLOPS = 2500.0   # dense fp16 MFMA: the ceiling of the exact NVFP4 path
 WORKLOADS = {"layer_decode": "LAYER_DECODE", "layer_skewed": "LAYER_SKEWED", "layer_prefill": "LAYER_PREFILL",
-             "layer_tiny": "TINY"}
+             "layer_tiny": "TINY", "layer_ep8": "LAYER_EP8", "layer_tp8": "LAYER_TP8"}
 
 
 def parse():
@@ -153,6 +154,41 @@ def grouped_gemm_decode(moe, torch, steps: int, copies: int = 8) -> dict:
             "hbm_frac": round(alg / us / 1e3 / HBM_PEAK_GBPS, 4), "weight_copies_rotated": copies}
 
 
+def dense_gemm(moe, torch, launches: int = 20) -> dict:
+    """The dense special case (one group, 8192^3, NONE epilogue) on packed weights."""
+    import synth
+    G = synth.GEMM_DENSE
+    dev = torch.device("cuda")
+    w = torch.from_numpy(synth.gemm_b(G, 0)).to(dev)
+    wq = torch.empty(1, G.N, G.K // 2, dtype=torch.uint8, device=dev)
+    wsf = torch.empty(1, G.N, G.K // 16, dtype=torch.uint8, device=dev)
+    wgs = torch.empty(1, dtype=torch.float32, device=dev)
+    moe.moe_quantize_nvfp4(w, wq[0], wsf[0], wgs, moe.MOE_GS_DYNAMIC)
+    del w
+    W = moe.pack_weights(moe.NVFP4Tensor(wq, wsf, wgs))
+    del wq, wsf
+    a_bits = torch.from_numpy(synth.gemm_a_bf16(G).view(np.int16)).to(dev).view(torch.bfloat16)
+    A = moe.quantize_alloc(a_bits)
+    del a_bits
+    off = torch.tensor([0, G.M], dtype=torch.int32, device=dev)
+    D = torch.empty(G.M, G.N, dtype=torch.bfloat16, device=dev)
+    args = moe._gemm_args_for(A, W, off, G.M, moe.MOE_EPI_NONE, D, None)
+    ws = moe._ws(moe.moe_grouped_gemm_nvfp4_workspace(args), dev)
+    for _ in range(3):
+        moe.moe_grouped_gemm_nvfp4(args, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(launches):
+        moe.moe_grouped_gemm_nvfp4(args, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / launches
+    flops = 2.0 * G.M * G.N * G.K
+    return {"workload": G.name, "avg_launch_us": round(us, 1), "tflops": round(flops / us / 1e6, 1),
+            "frac_of_f16_dense_peak": round(flops / us / 1e6 / F16_PEAK_TFLOPS, 4)}
+
+
 def cpu_baseline(L, offsets, row_src, seconds):
     """The oracle's grouped GEMMs (gate/up then down) over the routed rows of the first
     experts, one expert at a time until `seconds` of CPU time is spent; FLOPs / time."""
@@ -187,21 +223,10 @@ def cpu_baseline(L, offsets, row_src, seconds):
                       f"{spent:.1f} s of CPU time"}
 
 
-def main():
-    args = parse()
-    if args.copy_calibration_mib:
-        copy_calibration(args.copy_calibration_mib)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
-              file=sys.stderr)
-        sys.exit(2)
-    import torch
-
-    import block_scaled_fp4_02_amd as moe
+def run_layer(L, moe, torch, steps: int, warmup: int) -> dict:
+    """Time `steps` full layer steps (after `warmup`) with HIP events around every stage on
+    the launch stream; returns the stage times and the derived GEMM figures."""
     import synth
-    L = getattr(synth, WORKLOADS[args.workload])
-    torch.cuda.set_device(0)
     dev = torch.device("cuda")
     t_setup = time.time()
     W1, W2 = make_weights(L, moe, torch)
@@ -209,28 +234,28 @@ def main():
     x = torch.from_numpy(synth.layer_activations(L).view(np.int16)).to(dev).view(torch.bfloat16)
     plan = moe.MoELayerPlan(L.T, L.E, L.k, L.H, L.I, W1, W2)
     torch.cuda.synchronize()
-    print(f"# setup {time.time() - t_setup:.1f}s", file=sys.stderr, flush=True)
+    print(f"# {L.name}: setup {time.time() - t_setup:.1f}s", file=sys.stderr, flush=True)
 
     stages = ["route", "quantize_input", "gemm1", "requantize", "gemm2", "finalize"]
     calls = [lambda: plan.route(logits), lambda: plan.quantize_input(x), plan.gemm1, plan.requantize,
              plan.gemm2, plan.finalize]
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         plan.forward(logits, x)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         evs[s][0].record(stream)
         for i, c in enumerate(calls):
             c()
             evs[s][i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    stage_us = {st: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]) * 1e3)
+    ms_per_step = elapsed * 1e3 / steps
+    stage_us = {st: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)]) * 1e3)
                 for i, st in enumerate(stages)}
 
     off = plan.off.cpu().numpy()
@@ -246,16 +271,50 @@ def main():
     g1_alg_bytes = w1_bytes + x_bytes + act_bytes
     g1_s = stage_us["gemm1"] * 1e-6
     g2_s = stage_us["gemm2"] * 1e-6
-    value = (gemm1_flops + gemm2_flops) / (ms_per_step * 1e-3) / 1e12
     weight_gbps = (w1_bytes + w2_bytes) / (g1_s + g2_s) / 1e9
+    return {"plan": plan, "off": off, "sizes": sizes, "ms_per_step": ms_per_step, "stage_us": stage_us,
+            "value": (gemm1_flops + gemm2_flops) / (ms_per_step * 1e-3) / 1e12,
+            "gemm_tflops": (gemm1_flops + gemm2_flops) / (g1_s + g2_s) / 1e12,
+            "weight_gbps": weight_gbps, "g1_alg_bytes": g1_alg_bytes, "g1_s": g1_s}
+
+
+def shard_record(L, moe, torch, steps: int) -> dict:
+    """One GPU's share of the decode layer under expert or tensor parallelism, full path."""
+    r = run_layer(L, moe, torch, steps, 2)
+    out = {"workload": L.name, "ms_per_step": round(r["ms_per_step"], 4), "tflops": round(r["value"], 2),
+           "gemm_tflops": round(r["gemm_tflops"], 2), "weight_hbm_GBps": round(r["weight_gbps"], 1),
+           "weight_hbm_frac": round(r["weight_gbps"] / HBM_PEAK_GBPS, 4),
+           "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()}}
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_scaled_fp4_02_amd as moe
+    import synth
+    L = getattr(synth, WORKLOADS[args.workload])
+    torch.cuda.set_device(0)
+    r = run_layer(L, moe, torch, args.steps, args.warmup)
+    sizes, g1_s = r["sizes"], r["g1_s"]
     rec = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(r["value"], 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -267,19 +326,25 @@ def main():
                    "operands": "NVFP4 (e2m1, e4m3 scale per 16, f32 global) dequantised exactly to fp16 MFMA, fp32 accumulate",
                    "weights_layout": "packed"},
         "roofline": {"kernel": "gemm_lds_kernel<1> (gate/up + SwiGLU)", "bound": "hbm",
-                     "achieved": round(g1_alg_bytes / g1_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(g1_alg_bytes / g1_s / 1e9 / HBM_PEAK_GBPS, 4),
+                     "achieved": round(r["g1_alg_bytes"] / g1_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(r["g1_alg_bytes"] / g1_s / 1e9 / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic("moe::gemm::gemm_lds_kernel<1>") if L is synth.LAYER_DECODE else None,
-                     "alg_bytes_per_launch": int(g1_alg_bytes), "avg_launch_us": round(stage_us["gemm1"], 2)},
-        "gemm_tflops": round((gemm1_flops + gemm2_flops) / (g1_s + g2_s) / 1e12, 2),
-        "weight_hbm_GBps": round(weight_gbps, 1),
-        "weight_hbm_frac": round(weight_gbps / HBM_PEAK_GBPS, 4),
-        "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+                     "alg_bytes_per_launch": int(r["g1_alg_bytes"]), "avg_launch_us": round(g1_s * 1e6, 2)},
+        "gemm_tflops": round(r["gemm_tflops"], 2),
+        "weight_hbm_GBps": round(r["weight_gbps"], 1),
+        "weight_hbm_frac": round(r["weight_gbps"] / HBM_PEAK_GBPS, 4),
+        "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
     }
+    off, row_src = r["off"], r["plan"].row_src.cpu().numpy()
+    del r
+    torch.cuda.empty_cache()
     if L is synth.LAYER_DECODE:
         rec["grouped_gemm_decode_8x32"] = grouped_gemm_decode(moe, torch, args.steps)
+        rec["dense_gemm_8192"] = dense_gemm(moe, torch)
+        rec["shard_ep8"] = shard_record(synth.LAYER_EP8, moe, torch, args.steps)
+        rec["shard_tp8"] = shard_record(synth.LAYER_TP8, moe, torch, args.steps)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(L, off, plan.row_src.cpu().numpy(), args.cpu_baseline_seconds)
+        rec["cpu_baseline"] = cpu_baseline(L, off, row_src, args.cpu_baseline_seconds)
     print(json.dumps(rec), flush=True)
 
 

@@ -32,48 +32,64 @@ namespace {
 
 // ---- work list ---------------------------------------------------------------
 
+// One workgroup: per block of 1024 experts, chunk counts, an inclusive scan of the item
+// counts (wave scans plus a scan of the 16 wave totals), then every thread writes items
+// w = t, t + 1024, ... of the block, finding each item's expert by binary search over the
+// scan.  Item counts stay below 2^31 (the grid bound is checked on the host).
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restrict__ offsets, int E,
                                                         int64_t R, int chunk_rows, int n_tiles, int64_t max_items,
                                                         int4 *__restrict__ items,
                                                         int *__restrict__ count) {
-  __shared__ int64_t scan[1024];
-  int64_t carry = 0;
+  __shared__ int incl[1024];     // inclusive scan of the block's per-expert item counts
+  __shared__ int first_row[1024];
+  __shared__ int n_rows[1024];
+  __shared__ int wave_total[16];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  int carry = 0;
   for (int base = 0; base < E; base += 1024) {
-    const int e = base + static_cast<int>(threadIdx.x);
-    int64_t lo = 0, rows = 0;
+    const int e = base + t;
+    int lo = 0, rows = 0;
     if (e < E) {
-      lo = offsets[e];
-      lo = lo < 0 ? 0 : (lo > R ? R : lo);
-      int64_t hi = offsets[e + 1];
-      hi = hi < lo ? lo : (hi > R ? R : hi);
-      rows = hi - lo;
+      int64_t l = offsets[e];
+      l = l < 0 ? 0 : (l > R ? R : l);
+      int64_t h = offsets[e + 1];
+      h = h < l ? l : (h > R ? R : h);
+      lo = static_cast<int>(l);
+      rows = static_cast<int>(h - l);
     }
-    const int64_t chunks = (rows + chunk_rows - 1) / chunk_rows;
-    const int64_t mine = chunks * n_tiles;
-    scan[threadIdx.x] = mine;
+    const int mine = (rows + chunk_rows - 1) / chunk_rows * n_tiles;
+    int v = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(v, o, kWave);
+      if (lane >= o) v += u;
+    }
+    if (lane == 63) wave_total[wv] = v;
     __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-      const int64_t add = threadIdx.x >= static_cast<unsigned>(o) ? scan[threadIdx.x - o] : 0;
-      __syncthreads();
-      scan[threadIdx.x] += add;
-      __syncthreads();
-    }
-    const int64_t first = carry + scan[threadIdx.x] - mine;
-    for (int64_t nt = 0; nt < n_tiles; nt++) {
-      for (int64_t c = 0; c < chunks; c++) {
-        const int64_t w = first + nt * chunks + c;
-        if (w < max_items) {
-          const int64_t r0 = lo + c * chunk_rows;
-          const int64_t nr = rows - c * chunk_rows;
-          items[w] = make_int4(e, static_cast<int>(r0), static_cast<int>(nr < chunk_rows ? nr : chunk_rows),
-                               static_cast<int>(nt));
-        }
+    int before = 0;
+    for (int w = 0; w < wv; w++) before += wave_total[w];
+    incl[t] = before + v;
+    first_row[t] = lo;
+    n_rows[t] = rows;
+    __syncthreads();
+    const int block_items = incl[1023];
+    for (int w = t; w < block_items && carry + w < max_items; w += 1024) {
+      int a = 0, b = 1023;   // first expert slot with incl > w
+      while (a < b) {
+        const int m = (a + b) >> 1;
+        if (incl[m] > w) b = m;
+        else a = m + 1;
       }
+      const int chunks = (n_rows[a] + chunk_rows - 1) / chunk_rows;
+      const int local = w - (incl[a] - chunks * n_tiles);
+      const int nt = local / chunks, c = local % chunks;
+      const int nr = n_rows[a] - c * chunk_rows;
+      items[carry + w] = make_int4(base + a, first_row[a] + c * chunk_rows, nr < chunk_rows ? nr : chunk_rows, nt);
     }
-    carry += scan[1023];
+    carry += block_items;
     __syncthreads();
   }
-  if (threadIdx.x == 0) *count = static_cast<int>(carry < max_items ? carry : max_items);
+  if (t == 0) *count = static_cast<int>(carry < max_items ? carry : max_items);
 }
 
 // ---- the packed weight layout ---------------------------------------------------

@@ -62,6 +62,13 @@ LAYER_DECODE = Layer("layer_decode_t1024_e256_k8_h6144_i2048", T=1024, E=256, k=
 LAYER_SKEWED = Layer("layer_skewed_t512_e256_k8_h6144_i2048_zipf1.1", T=512, E=256, k=8, H=6144,
                      I=2048, zipf_beta=0.37)
 LAYER_PREFILL = Layer("layer_prefill_t16384_e256_k8_h6144_i2048", T=16384, E=256, k=8, H=6144, I=2048)
+# One GPU's share of the decode layer under 8-way expert parallelism (32 local experts,
+# ~32 rows each, as many rows as tokens x top-8 / 8) and under 8-way tensor parallelism
+# (all 256 experts, intermediate 2048 / 8 = 256 per GPU).
+LAYER_EP8 = Layer("layer_ep8_share_t128_e32_k8_h6144_i2048", T=128, E=32, k=8, H=6144, I=2048)
+LAYER_TP8 = Layer("layer_tp8_share_t1024_e256_k8_h6144_i256", T=1024, E=256, k=8, H=6144, I=256)
+# The dense special case: one group, large square GEMM.
+GEMM_DENSE = Gemm("dense_gemm_e1_m8192_k8192_n8192", E=1, M=8192, K=8192, N=8192)
 
 ZIPF_S = 1.1
 

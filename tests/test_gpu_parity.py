@@ -232,6 +232,30 @@ def test_gemm_none_decode_grouped_gemm_full(packed):
     _run_gemm_none(A, Bs, off, None, G.E * G.M, "decode 8x32x6144x2048", packed)
 
 
+def test_gemm_dense_small_full():
+    """One group (a plain dense GEMM): every output element against the oracle."""
+    A, Bs, off, A_rows, R = _gemm_case([512], 1024, 512, False, seed=11)
+    _run_gemm_none(A, Bs, off, A_rows, R, "dense 512x512x1024", packed=True)
+
+
+@pytest.mark.timeout(600)
+def test_gemm_dense_full_size_sampled():
+    """The dense 8192^3 case in the benchmark's launch configuration, on sampled rows."""
+    G = synth.GEMM_DENSE
+    log("dense 8192^3: quantising operands (oracle)")
+    A = oracle.quantize_bf16(synth.gemm_a_bf16(G))
+    B = oracle.quantize(synth.gemm_b(G, 0))
+    Bq, Bsf, gB = stack([B])
+    off = np.array([0, G.M], np.int32)
+    dA = moe.NVFP4Tensor(dev(A.q), dev(A.sf), dev(np.array([A.g], np.float32)))
+    D = moe.grouped_gemm_alloc(dA, _weights(Bq, Bsf, gB, True), dev(off), G.M, moe.MOE_EPI_NONE)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(5).choice(G.M, 48, replace=False)).astype(np.int32)
+    log("dense 8192^3: oracle on sampled rows")
+    ref = oracle.grouped_gemm(A, Bq, Bsf, gB, off, rows=rows)
+    check_bf16(host_bits(D)[rows], ref, "dense 8192^3 sampled rows")
+
+
 def _pack_reference(q: np.ndarray, sf: np.ndarray) -> np.ndarray:
     """The packed layout written out from its definition in the header (byte moves only)."""
     rows, half_k = q.shape
@@ -353,7 +377,8 @@ def test_layer_tiny_end_to_end(packed):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("L", [synth.LAYER_DECODE, synth.LAYER_SKEWED], ids=lambda L: L.name)
+@pytest.mark.parametrize("L", [synth.LAYER_DECODE, synth.LAYER_SKEWED, synth.LAYER_EP8, synth.LAYER_TP8],
+                         ids=lambda L: L.name)
 def test_layer_full_size_end_to_end(L):
     W1, W2, d1, d2 = layer_weights(L)
     logits, x = synth.router_logits(L), synth.layer_activations(L)
