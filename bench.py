@@ -223,16 +223,22 @@ def cpu_baseline(L, offsets, row_src, seconds):
                       f"{spent:.1f} s of CPU time"}
 
 
-def run_layer(L, moe, torch, steps: int, warmup: int) -> dict:
+def run_layer(L, moe, torch, steps: int, warmup: int, weights=None, fused: bool = False) -> dict:
     """Time `steps` full layer steps (after `warmup`) with HIP events around every stage on
-    the launch stream; returns the stage times and the derived GEMM figures."""
+    the launch stream; returns the stage times and the derived GEMM figures.  fused: requantise
+    the SwiGLU output in the gate/up GEMM's epilogue with a static global scale, calibrated
+    as a caller would, from one dynamic pass."""
     import synth
     dev = torch.device("cuda")
     t_setup = time.time()
-    W1, W2 = make_weights(L, moe, torch)
+    W1, W2 = weights if weights is not None else make_weights(L, moe, torch)
     logits = torch.from_numpy(synth.router_logits(L)).to(dev)
     x = torch.from_numpy(synth.layer_activations(L).view(np.int16)).to(dev).view(torch.bfloat16)
     plan = moe.MoELayerPlan(L.T, L.E, L.k, L.H, L.I, W1, W2)
+    if fused:
+        plan.forward(logits, x)
+        g2 = plan.actq.gs.clone()
+        plan = moe.MoELayerPlan(L.T, L.E, L.k, L.H, L.I, W1, W2, static_g2=g2)
     torch.cuda.synchronize()
     print(f"# {L.name}: setup {time.time() - t_setup:.1f}s", file=sys.stderr, flush=True)
 
@@ -272,7 +278,8 @@ def run_layer(L, moe, torch, steps: int, warmup: int) -> dict:
     g1_s = stage_us["gemm1"] * 1e-6
     g2_s = stage_us["gemm2"] * 1e-6
     weight_gbps = (w1_bytes + w2_bytes) / (g1_s + g2_s) / 1e9
-    return {"plan": plan, "off": off, "sizes": sizes, "ms_per_step": ms_per_step, "stage_us": stage_us,
+    return {"plan": plan, "weights": (W1, W2), "off": off, "sizes": sizes, "ms_per_step": ms_per_step,
+            "stage_us": stage_us,
             "value": (gemm1_flops + gemm2_flops) / (ms_per_step * 1e-3) / 1e12,
             "gemm_tflops": (gemm1_flops + gemm2_flops) / (g1_s + g2_s) / 1e12,
             "weight_gbps": weight_gbps, "g1_alg_bytes": g1_alg_bytes, "g1_s": g1_s}
@@ -336,6 +343,14 @@ def main():
         "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
     }
     off, row_src = r["off"], r["plan"].row_src.cpu().numpy()
+    if L is synth.LAYER_DECODE:
+        f = run_layer(L, moe, torch, args.steps, args.warmup, weights=r["weights"], fused=True)
+        rec["layer_decode_fused_static_g2"] = {
+            "ms_per_step": round(f["ms_per_step"], 4), "tflops": round(f["value"], 2),
+            "stage_us": {k: round(v, 2) for k, v in f["stage_us"].items()},
+            "note": "SwiGLU output requantised in the gate/up GEMM epilogue (MOE_EPI_SWIGLU_NVFP4) with a "
+                    "static global scale calibrated from one dynamic pass; requantize stage is empty"}
+        del f
     del r
     torch.cuda.empty_cache()
     if L is synth.LAYER_DECODE:

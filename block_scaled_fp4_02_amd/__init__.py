@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_nvfp4.so")
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
 MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
 MOE_GS_STATIC, MOE_GS_DYNAMIC = 0, 1
-MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
+MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_NVFP4 = 0, 1, 2
 MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_PACKED = 0, 1
 
 EXPORTED = [
@@ -56,6 +56,7 @@ class moe_gemm_args(C.Structure):
         ("epilogue", C.c_int32),
         ("D", C.c_void_p), ("amax_out", C.c_void_p),
         ("B_layout", C.c_int32),
+        ("D_sf", C.c_void_p), ("D_gs", C.c_void_p),
     ]
 
 
@@ -136,10 +137,10 @@ def moe_quantize_nvfp4(x, q, sf, gs, gs_mode=MOE_GS_DYNAMIC, amax_in=None, ws=No
 
 
 def make_gemm_args(A, A_sf, A_gs, B, B_sf, B_gs, expert_offsets, R, epilogue, D=None,
-                   amax_out=None, A_rows=None, N=None, K=None) -> moe_gemm_args:
+                   amax_out=None, A_rows=None, N=None, K=None, D_sf=None, D_gs=None) -> moe_gemm_args:
     """B / B_sf are row-major NVFP4 [E, N, K/2] / [E, N, K/16]; pass B_sf=None and B as the
     packed buffer [E, N*K*9/16 bytes] (moe_pack_weights_nvfp4) with N and K for the packed
-    layout."""
+    layout.  D_sf / D_gs: scales and static global scale of D (SWIGLU_NVFP4 only)."""
     packed = B_sf is None
     if packed:
         E = B.shape[0]
@@ -153,6 +154,7 @@ def make_gemm_args(A, A_sf, A_gs, B, B_sf, B_gs, expert_offsets, R, epilogue, D=
     a.E, a.N, a.K, a.R, a.epilogue = E, N, K, int(R), epilogue
     a.D, a.amax_out = _p(D), _p(amax_out)
     a.B_layout = MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_ROWMAJOR
+    a.D_sf, a.D_gs = _p(D_sf), _p(D_gs)
     return a
 
 
@@ -249,11 +251,20 @@ def _gemm_args_for(A: NVFP4Tensor, B, expert_offsets, R, epilogue, D, A_rows):
 
 
 def grouped_gemm_alloc(A: NVFP4Tensor, B, expert_offsets, R, epilogue=MOE_EPI_NONE,
-                       A_rows=None, stream=None):
+                       A_rows=None, stream=None, D_gs=None):
     """B: NVFP4Tensor (row-major) or PackedWeights.  Returns D (and the partial-maxima tensor
-    for SWIGLU)."""
+    for SWIGLU; an NVFP4Tensor with global scale D_gs for SWIGLU_NVFP4)."""
     N = B.N if isinstance(B, PackedWeights) else B.q.shape[1]
     dev = A.q.device
+    if epilogue == MOE_EPI_SWIGLU_NVFP4:
+        I = N // 2
+        Dq = NVFP4Tensor(torch.empty(int(R), I // 2, dtype=torch.uint8, device=dev),
+                         torch.empty(int(R), I // 16, dtype=torch.uint8, device=dev), D_gs)
+        a = _gemm_args_for(A, B, expert_offsets, R, epilogue, Dq.q, A_rows)
+        a.D_sf, a.D_gs = _p(Dq.sf), _p(D_gs)
+        _check("moe_grouped_gemm_nvfp4_can_implement", moe_grouped_gemm_nvfp4_can_implement(a))
+        moe_grouped_gemm_nvfp4(a, _ws(moe_grouped_gemm_nvfp4_workspace(a), dev), stream)
+        return Dq
     cols = N if epilogue == MOE_EPI_NONE else N // 2
     D = torch.empty(int(R), cols, dtype=torch.bfloat16, device=dev)
     a = _gemm_args_for(A, B, expert_offsets, R, epilogue, D, A_rows)
@@ -271,8 +282,11 @@ class MoELayerPlan:
     """Pre-allocated buffers and argument blocks for repeated forward passes of one layer
     shape (what a serving loop or a benchmark reuses): no allocation per call."""
 
-    def __init__(self, T: int, E: int, k: int, H: int, I: int, W1, W2, device="cuda"):
-        """W1 / W2: NVFP4Tensor (row-major) or PackedWeights (the fast decode layout)."""
+    def __init__(self, T: int, E: int, k: int, H: int, I: int, W1, W2, device="cuda", static_g2=None):
+        """W1 / W2: NVFP4Tensor (row-major) or PackedWeights (the fast decode layout).
+        static_g2: a caller-calibrated global scale (one-element f32 device tensor) for the
+        SwiGLU output; with it the gate/up GEMM requantises in its epilogue
+        (MOE_EPI_SWIGLU_NVFP4) and requantize() does nothing."""
         self.T, self.E, self.k, self.H, self.I = T, E, k, H, I
         R = T * k
         self.R = R
@@ -286,9 +300,15 @@ class MoELayerPlan:
         self.Y = z(R, H, dt=torch.bfloat16)
         self.out = z(T, H, dt=torch.bfloat16)
         self.W1, self.W2 = W1, W2
-        self.args1 = _gemm_args_for(self.xq, W1, self.off, R, MOE_EPI_SWIGLU, self.act, self.row_src)
-        self.amax = z(max(moe_grouped_gemm_nvfp4_amax_slots(self.args1), 1), dt=torch.float32)
-        self.args1.amax_out = _p(self.amax)
+        self.fused = static_g2 is not None
+        if self.fused:
+            self.actq.gs.copy_(static_g2.reshape(1))
+            self.args1 = _gemm_args_for(self.xq, W1, self.off, R, MOE_EPI_SWIGLU_NVFP4, self.actq.q, self.row_src)
+            self.args1.D_sf, self.args1.D_gs = _p(self.actq.sf), _p(self.actq.gs)
+        else:
+            self.args1 = _gemm_args_for(self.xq, W1, self.off, R, MOE_EPI_SWIGLU, self.act, self.row_src)
+            self.amax = z(max(moe_grouped_gemm_nvfp4_amax_slots(self.args1), 1), dt=torch.float32)
+            self.args1.amax_out = _p(self.amax)
         self.args2 = _gemm_args_for(self.actq, W2, self.off, R, MOE_EPI_NONE, self.Y, None)
         for a in (self.args1, self.args2):
             _check("moe_grouped_gemm_nvfp4_can_implement", moe_grouped_gemm_nvfp4_can_implement(a))
@@ -311,6 +331,8 @@ class MoELayerPlan:
         moe_grouped_gemm_nvfp4(self.args1, self.ws_g1, stream)
 
     def requantize(self, stream=None):
+        if self.fused:   # done in the gate/up GEMM's epilogue
+            return
         moe_quantize_nvfp4(self.act, self.actq.q, self.actq.sf, self.actq.gs, MOE_GS_DYNAMIC, self.amax,
                            self.ws_q2, stream)
 

@@ -11,6 +11,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "nvfp4_round.hpp"
 
 namespace moe {
 namespace gemm {
@@ -37,6 +38,8 @@ struct Params {
   const int32_t *offsets;
   int64_t R;
   int chunk_rows, n_tiles;
+  uint8_t *D_sf;        // SwiGLU + NVFP4 epilogue: scales of D, and the static global scale
+  const float *D_gs;
 };
 
 // Largest expert count for which waves derive their work item from the offsets themselves
@@ -227,6 +230,42 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float gate_acc, float up_acc) {
   const float up = round_bf16(up_acc);
   const float silu = gate * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gate * -1.4426950408889634f));
   return f32_to_bf16(silu * up);
+}
+
+// SwiGLU + NVFP4 epilogue for one token row and one 16-column block of act in the 16x16
+// MFMA D layout, where lane group g holds the block's columns 4g .. 4g + 3 (gate and up
+// accumulators of those columns, already summed).  The bf16 SwiGLU values are quantised
+// with the static global scale g2 by exactly the steps of the quantiser (binary32, no
+// contraction): the four lanes of the row exchange their block maxima, each packs its four
+// codes into two bytes, lane group 0 writes the scale byte.  All lanes of the wave execute
+// it (the shuffles pair lanes of the same row); `store` only predicates the writes.
+__device__ __forceinline__ void swiglu_nvfp4_block(const float4v &gate, const float4v &up, float gscale, float g2,
+                                                   bool store, uint8_t *codes, uint8_t *scale, int g) {
+#pragma clang fp contract(off)
+  float v[4];
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    v[c] = bf16_to_f32(swiglu_bf16(gate[c] * gscale, up[c] * gscale));
+    amax = fmaxf(amax, fabsf(v[c]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+  const float six_g = 6.0f * g2;
+  const float t = fminf(amax / six_g, 448.0f);
+  const uint32_t s = e4m3_rne(t);
+  const float sg = e4m3_value(s) * g2;
+  uint32_t packed = 0u;
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const uint32_t sign = (__float_as_uint(v[c]) >> 31) << 3;
+    const uint32_t mag = (s != 0u) ? e2m1_rne(fminf(fabsf(v[c]) / sg, 6.0f)) : 0u;
+    packed |= (sign | mag) << (4 * c);
+  }
+  if (store) {
+    *reinterpret_cast<uint16_t *>(codes + 2 * g) = static_cast<uint16_t>(packed);
+    if (g == 0) *scale = static_cast<uint8_t>(s);
+  }
 }
 
 // ---- launchers (one per kernel family) -------------------------------------------------

@@ -45,7 +45,7 @@ __device__ __forceinline__ void ks_body(const Params &P, float *red, float *wmax
   int nrow[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    if (EPI == MOE_EPI_SWIGLU) {
+    if (EPI != MOE_EPI_NONE) {
       const int gate = nt * (SPAN / 2) + ng * 32 + (j & 1) * 16;
       nrow[j] = (j >= 2) ? I + gate : gate;
     } else {
@@ -160,6 +160,23 @@ __device__ __forceinline__ void ks_body(const Params &P, float *red, float *wmax
 
   // epilogue: 16x16 D lane layout -- weight row 4g + i, token row r of the tile
   const float gscale = (*P.A_gs) * P.B_gs[e];
+  if constexpr (EPI == MOE_EPI_SWIGLU_NVFP4) {
+    if (kq == 0) {   // wave-uniform
+      const float g2 = *P.D_gs;
+#pragma unroll
+      for (int mt = 0; mt < NM; mt++) {
+        const int m = mt * 16 + r;
+        const int64_t p = row0 + (m < nrows ? m : 0);
+#pragma unroll
+        for (int jp = 0; jp < 2; jp++) {
+          const int blk = nrow[jp] / 16;
+          swiglu_nvfp4_block(acc[jp][mt], acc[2 + jp][mt], gscale, g2, m < nrows,
+                             static_cast<uint8_t *>(P.D) + p * (I / 2) + blk * 8, P.D_sf + p * (I / 16) + blk, g);
+        }
+      }
+    }
+    return;
+  }
   float amax = 0.f;
   if (kq == 0) {
 #pragma unroll
@@ -236,6 +253,7 @@ int ksplit_waves(int ks) { return ks < 4 ? 4 : ks; }
 
 void launch_ksplit(const Params &p, int epi, int ks, dim3 grid, hipStream_t stream) {
   if (epi == MOE_EPI_SWIGLU) launch_epi<MOE_EPI_SWIGLU>(p, ks, grid, stream);
+  else if (epi == MOE_EPI_SWIGLU_NVFP4) launch_epi<MOE_EPI_SWIGLU_NVFP4>(p, ks, grid, stream);
   else launch_epi<MOE_EPI_NONE>(p, ks, grid, stream);
 }
 

@@ -54,7 +54,7 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT> &sh, i
   int nrow[4];   // first weight row of the wave's four tiles (SwiGLU: gate, gate, up, up)
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    if (EPI == MOE_EPI_SWIGLU) {
+    if (EPI != MOE_EPI_NONE) {
       const int gate = nt * (SPAN / 2) + wv * 32 + (j & 1) * 16;
       nrow[j] = (j >= 2) ? I + gate : gate;
     } else {
@@ -169,6 +169,21 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT> &sh, i
 
   // epilogue: 16x16 D lane layout -- weight row 4g + i, token row r of the tile
   const float gscale = (*P.A_gs) * P.B_gs[e];
+  if constexpr (EPI == MOE_EPI_SWIGLU_NVFP4) {
+    const float g2 = *P.D_gs;
+#pragma unroll
+    for (int mt = 0; mt < NM; mt++) {
+      const int m = mt * 16 + r;
+      const int64_t p = row0 + (m < nrows ? m : 0);
+#pragma unroll
+      for (int jp = 0; jp < 2; jp++) {
+        const int blk = nrow[jp] / 16;
+        swiglu_nvfp4_block(acc[jp][mt], acc[2 + jp][mt], gscale, g2, m < nrows,
+                           static_cast<uint8_t *>(P.D) + p * (I / 2) + blk * 8, P.D_sf + p * (I / 16) + blk, g);
+      }
+    }
+    return;
+  }
   float amax = 0.f;
 #pragma unroll
   for (int mt = 0; mt < NM; mt++) {
@@ -229,6 +244,8 @@ __global__ __launch_bounds__(256, 3) void gemm_lds_kernel(Params P) {
 void launch_lds(const Params &p, int epi, dim3 grid, hipStream_t stream) {
   const dim3 block(256);
   if (epi == MOE_EPI_SWIGLU) hipLaunchKernelGGL(gemm_lds_kernel<MOE_EPI_SWIGLU>, grid, block, 0, stream, p);
+  else if (epi == MOE_EPI_SWIGLU_NVFP4)
+    hipLaunchKernelGGL(gemm_lds_kernel<MOE_EPI_SWIGLU_NVFP4>, grid, block, 0, stream, p);
   else hipLaunchKernelGGL(gemm_lds_kernel<MOE_EPI_NONE>, grid, block, 0, stream, p);
 }
 

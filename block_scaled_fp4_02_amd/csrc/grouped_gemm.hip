@@ -189,7 +189,8 @@ hipError_t launch_grouped_gemm(const moe_gemm_args &a, const GemmPlan &plan, voi
                        plan.chunk_rows, plan.n_tiles, plan.max_items, items, count);
   }
   const Params p{a.A, a.A_sf, a.A_gs, a.A_rows, a.rows_A, a.B, a.B_sf, a.B_gs, a.E, a.N, a.K,
-                 a.D, a.amax_out, items, count, a.expert_offsets, a.R, plan.chunk_rows, plan.n_tiles};
+                 a.D, a.amax_out, items, count, a.expert_offsets, a.R, plan.chunk_rows, plan.n_tiles,
+                 a.D_sf, a.D_gs};
   const dim3 grid(static_cast<uint32_t>(plan.grid));
   switch (plan.kernel) {
     case kLds: launch_lds(p, a.epilogue, grid, stream); break;

@@ -21,8 +21,10 @@ moe_status check_gemm(const moe_gemm_args *a, bool need_pointers) {
   if (a->E < 1 || a->E > 65536 || a->N < 1 || a->K < 1 || a->R < 0 || a->R >= (int64_t(1) << 31) ||
       a->rows_A < 0)
     return MOE_ERR_SHAPE;
-  if (a->epilogue != MOE_EPI_NONE && a->epilogue != MOE_EPI_SWIGLU) return MOE_ERR_UNSUPPORTED;
+  if (a->epilogue != MOE_EPI_NONE && a->epilogue != MOE_EPI_SWIGLU && a->epilogue != MOE_EPI_SWIGLU_NVFP4)
+    return MOE_ERR_UNSUPPORTED;
   if (a->B_layout != MOE_LAYOUT_ROWMAJOR && a->B_layout != MOE_LAYOUT_PACKED) return MOE_ERR_UNSUPPORTED;
+  if (a->epilogue == MOE_EPI_SWIGLU_NVFP4 && a->B_layout != MOE_LAYOUT_PACKED) return MOE_ERR_UNSUPPORTED;
   if (a->K % 16 != 0) return MOE_ERR_SHAPE;
   if (a->K % 256 != 0 || a->N % 256 != 0) return MOE_ERR_UNSUPPORTED;
   if (a->R > 0 && a->rows_A < 1) return MOE_ERR_SHAPE;
@@ -40,6 +42,7 @@ moe_status check_gemm(const moe_gemm_args *a, bool need_pointers) {
     if (a->B_layout == MOE_LAYOUT_ROWMAJOR && !a->B_sf) return MOE_ERR_NULL;
     if (a->R > 0 && (!a->A || !a->A_sf || !a->D)) return MOE_ERR_NULL;
     if (a->epilogue == MOE_EPI_SWIGLU && !a->amax_out) return MOE_ERR_NULL;
+    if (a->epilogue == MOE_EPI_SWIGLU_NVFP4 && (!a->D_gs || (a->R > 0 && !a->D_sf))) return MOE_ERR_NULL;
   }
   return MOE_OK;
 }

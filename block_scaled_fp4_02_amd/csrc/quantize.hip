@@ -14,6 +14,7 @@
 // (order-free, so every workgroup sees the same g) and then quantises.  Memory-bound:
 // reads 2 (bf16) or 4 (f32) bytes and writes 0.5625 bytes per element.
 #include "common.hpp"
+#include "nvfp4_round.hpp"
 
 #pragma clang fp contract(off)
 
@@ -56,29 +57,6 @@ __global__ __launch_bounds__(256) void amax_kernel(const void *__restrict__ x, i
   if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) parts[blockIdx.x] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
-}
-
-// Nearest E4M3FN code to t in [0, 448], ties to the even code.
-__device__ __forceinline__ uint32_t e4m3_rne(float t) {
-  if (t < 0.015625f) return static_cast<uint32_t>(rintf(t * 512.0f));  // multiples of 2^-9
-  uint32_t u = __float_as_uint(t);
-  u += 0x7ffffu + ((u >> 20) & 1u);  // round the 23-bit mantissa to 3 bits, ties to even
-  return (u >> 20) - (120u << 3);    // rebias the exponent from 127 to 7
-}
-
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  if (c < 8u) return static_cast<float>(c) * 0.001953125f;  // subnormal: c * 2^-9
-  return __uint_as_float((((c >> 3) + 120u) << 23) | ((c & 7u) << 20));
-}
-
-// E2M1 magnitude code for u in [0, 6], ties to the even code.  Below 1 the E2M1 values are
-// the multiples of 0.5 (code = 2u rounded to nearest even); from 1 up they have one mantissa
-// bit, so the binary32 mantissa is rounded to one bit and the exponent rebiased (127 -> 1).
-__device__ __forceinline__ uint32_t e2m1_rne(float u) {
-  if (u < 1.0f) return static_cast<uint32_t>(rintf(u * 2.0f));
-  uint32_t b = __float_as_uint(u);
-  b += 0x1fffffu + ((b >> 22) & 1u);
-  return (b >> 22) - (126u << 1);
 }
 
 __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, int x_dtype,

@@ -143,6 +143,16 @@ moe_status moe_quantize_nvfp4(const void *x, int x_dtype, int64_t rows, int64_t 
  *                   amax_out[moe_grouped_gemm_nvfp4_amax_slots(args)] f32 receives
  *                   partial maxima of |D| (their maximum is max|D|; unused slots 0),
  *                   for moe_quantize_nvfp4(..., amax_in = amax_out, ...).
+ *   MOE_EPI_SWIGLU_NVFP4  the SwiGLU epilogue fused with NVFP4 quantisation of its bf16
+ *                   result under a static, caller-calibrated global scale g2 = *D_gs
+ *                   (device f32): D u8 [R, I/2] codes, D_sf u8 [R, I/16] E4M3 scales, with
+ *                   exactly the steps of moe_quantize_nvfp4 in MOE_GS_STATIC mode (the
+ *                   output equals SWIGLU followed by that call byte for byte).  A fused
+ *                   gate/up epilogue that requantises in one pass is the "next" step after
+ *                   the pages' FINALIZE/NONE epilogue modes ("The Epilogue That Broke the
+ *                   Kernel", "The Insight: FINALIZE vs NONE"); the static scale replaces the
+ *                   dynamic per-tensor amax, which needs a pass over all rows.  Packed
+ *                   weights only; amax_out is not used.
  * Rows p >= expert_offsets[E] of D are not written.
  * B_layout MOE_LAYOUT_ROWMAJOR: B / B_sf as above.  MOE_LAYOUT_PACKED: B is the output of
  * moe_pack_weights_nvfp4 for the E*N weight rows (B_sf is ignored and may be NULL); this is
@@ -154,7 +164,7 @@ moe_status moe_quantize_nvfp4(const void *x, int x_dtype, int64_t rows, int64_t 
  * launch is supported; a supported launch then cannot fail on its
  * configuration.  ws: moe_grouped_gemm_nvfp4_workspace(args) bytes.
  * ------------------------------------------------------------------------- */
-typedef enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1 } moe_epilogue;
+typedef enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_SWIGLU_NVFP4 = 2 } moe_epilogue;
 typedef enum moe_layout { MOE_LAYOUT_ROWMAJOR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout;
 
 typedef struct moe_gemm_args {
@@ -170,9 +180,12 @@ typedef struct moe_gemm_args {
   int32_t E, N, K;
   int64_t R;
   int32_t epilogue;               /* moe_epilogue */
-  void *D;                        /* bf16 [R, N] (NONE) or [R, N/2] (SWIGLU) */
+  void *D;                        /* bf16 [R, N] (NONE), bf16 [R, N/2] (SWIGLU),
+                                     u8 codes [R, N/4] (SWIGLU_NVFP4) */
   float *amax_out;                /* SWIGLU only */
   int32_t B_layout;               /* moe_layout */
+  uint8_t *D_sf;                  /* SWIGLU_NVFP4 only: u8 scales [R, N/32] */
+  const float *D_gs;              /* SWIGLU_NVFP4 only: static global scale g2 (one f32) */
 } moe_gemm_args;
 
 size_t moe_grouped_gemm_nvfp4_workspace(const moe_gemm_args *args);

@@ -207,10 +207,12 @@ class LayerResult:
     pass
 
 
-def moe_layer(logits, x_bf16, W1: list, W2: list, k: int) -> LayerResult:
+def moe_layer(logits, x_bf16, W1: list, W2: list, k: int, act_g: float | None = None) -> LayerResult:
     """The MoE layer step by step: route, permute, quantise x, GEMM1, SwiGLU,
     requantise, GEMM2, FINALIZE.  W1[e] / W2[e] are NVFP4 weights of expert e
-    ([2I, H] and [H, I]).  Returns every intermediate."""
+    ([2I, H] and [H, I]).  act_g: a static global scale for the requantisation of the
+    SwiGLU output (the fused-epilogue mode); None for the dynamic per-tensor scale.
+    Returns every intermediate."""
     E = len(W1)
     r = LayerResult()
     r.ids, r.w = route(logits, k)
@@ -220,7 +222,7 @@ def moe_layer(logits, x_bf16, W1: list, W2: list, k: int) -> LayerResult:
     g1 = np.array([w.g for w in W1], np.float32)
     r.y1 = grouped_gemm(r.xq, B1q, B1s, g1, r.offsets, A_rows=r.row_src)
     r.act = swiglu(r.y1)
-    r.actq = quantize_bf16(r.act)
+    r.actq = quantize_bf16(r.act, g=act_g)
     B2q = np.stack([w.q for w in W2]); B2s = np.stack([w.sf for w in W2])
     g2 = np.array([w.g for w in W2], np.float32)
     r.y2 = grouped_gemm(r.actq, B2q, B2s, g2, r.offsets)

@@ -67,11 +67,11 @@ def test_quantize_validation():
     assert q(4, 32, ws_bytes=0) == moe.MOE_ERR_WORKSPACE
 
 
-def gemm_args(E=8, N=2048, K=6144, R=256, epi=0, null=None):
+def gemm_args(E=8, N=2048, K=6144, R=256, epi=0, null=None, layout=0):
     a = moe.moe_gemm_args()
-    for f in ("A", "A_sf", "A_gs", "B", "B_sf", "B_gs", "expert_offsets", "D", "amax_out"):
+    for f in ("A", "A_sf", "A_gs", "B", "B_sf", "B_gs", "expert_offsets", "D", "amax_out", "D_sf", "D_gs"):
         setattr(a, f, FAKE)
-    a.rows_A, a.E, a.N, a.K, a.R, a.epilogue = R, E, N, K, R, epi
+    a.rows_A, a.E, a.N, a.K, a.R, a.epilogue, a.B_layout = R, E, N, K, R, epi, layout
     if null:
         setattr(a, null, None)
     return a
@@ -90,6 +90,9 @@ def test_gemm_can_implement_is_truthful_on_shapes():
         (dict(E=0), moe.MOE_ERR_SHAPE),
         (dict(R=-1), moe.MOE_ERR_SHAPE),
         (dict(epi=5), moe.MOE_ERR_UNSUPPORTED),
+        (dict(epi=2), moe.MOE_ERR_UNSUPPORTED),      # SwiGLU + NVFP4 needs packed weights
+        (dict(epi=2, layout=1, null="D_gs"), moe.MOE_ERR_NULL),
+        (dict(epi=2, layout=1, null="D_sf"), moe.MOE_ERR_NULL),
         (dict(null="B"), moe.MOE_ERR_NULL),
         (dict(null="expert_offsets"), moe.MOE_ERR_NULL),
         (dict(null="D"), moe.MOE_ERR_NULL),
@@ -100,6 +103,8 @@ def test_gemm_can_implement_is_truthful_on_shapes():
         assert L.moe_grouped_gemm_nvfp4_can_implement(C.byref(a)) == want, kw
         assert L.moe_grouped_gemm_nvfp4(C.byref(a), FAKE, 1 << 30, None) == want, kw
     assert L.moe_grouped_gemm_nvfp4_can_implement(None) == moe.MOE_ERR_NULL
+    # SwiGLU + NVFP4 with packed weights and all its pointers is supported
+    assert L.moe_grouped_gemm_nvfp4_can_implement(C.byref(gemm_args(epi=2, layout=1))) == moe.MOE_OK
     # amax_out is only needed by the SwiGLU epilogue
     assert L.moe_grouped_gemm_nvfp4_can_implement(C.byref(gemm_args(null="amax_out"))) == moe.MOE_OK
     # a short workspace is refused before any launch

@@ -320,6 +320,39 @@ def test_gemm_swiglu_shapes(sizes, K, I, packed):
     _run_gemm_swiglu(A, Bs, off, A_rows, R, f"sizes={sizes}", packed=packed)
 
 
+@pytest.mark.parametrize("sizes,K,I,g_div", [([8, 6, 9, 9], 256, 256, 1.0), ([0, 17, 33, 64, 65, 1], 512, 384, 4.0),
+                                             ([40] * 256 + [3, 0, 64], 256, 512, 1.0),   # LDS kernel
+                                             ([20, 32], 2048, 256, 1.0)])                # K split 8 ways
+def test_gemm_swiglu_nvfp4_fused(sizes, K, I, g_div):
+    """SwiGLU + NVFP4 epilogue with a static global scale g2: codes and scales equal the
+    oracle's static-scale quantisation of the GPU's own SwiGLU output byte for byte (same
+    decision in the same precision); against the oracle's own FP64 pipeline only elements
+    whose bf16 act differs by an ulp may change code.  g_div > 1 makes g2 small enough
+    that some blocks saturate."""
+    A, Bs, off, A_rows, R = _gemm_case(sizes, K, 2 * I, True, seed=17 + K + I)
+    Bq, Bsf, gB = stack(Bs)
+    dA = moe.NVFP4Tensor(dev(A.q), dev(A.sf), dev(np.array([A.g], np.float32)))
+    dB = _weights(Bq, Bsf, gB, True)
+    act, _ = moe.grouped_gemm_alloc(dA, dB, dev(off), R, moe.MOE_EPI_SWIGLU, A_rows=dev(A_rows))
+    act_bits = host_bits(act)
+    g2 = np.float32(max(np.abs(bf16_values(act_bits)).max(initial=0.0), 1e-30) / 2688.0 / g_div)
+    log(f"gemm SWIGLU_NVFP4 sizes={sizes} K={K} I={I} g2={g2:.4g}")
+    fused = moe.grouped_gemm_alloc(dA, dB, dev(off), R, moe.MOE_EPI_SWIGLU_NVFP4, A_rows=dev(A_rows),
+                                   D_gs=dev(np.array([g2], np.float32)))
+    torch.cuda.synchronize()
+    ref = oracle.quantize_bf16(act_bits, g=float(g2))
+    assert np.array_equal(fused.q.cpu().numpy(), ref.q)
+    assert np.array_equal(fused.sf.cpu().numpy(), ref.sf)
+    # the oracle's own pipeline: FP64 GEMM, SwiGLU, then the same static quantisation
+    y1 = oracle.grouped_gemm(A, Bq, Bsf, gB, off, A_rows=A_rows)
+    ref64 = oracle.quantize_bf16(oracle.swiglu(y1), g=float(g2))
+    same_act = (act_bits == oracle.swiglu(y1))
+    diff_codes = fused.q.cpu().numpy() != ref64.q
+    print(f"  codes differing from the FP64 pipeline: {diff_codes.mean():.2e} "
+          f"(act bf16 differs in {1 - same_act.mean():.2e})", flush=True)
+    assert diff_codes.mean() <= 2 * (1 - same_act.mean()) + 1e-3
+
+
 def test_requantize_bit_exact_from_partials():
     rng = np.random.default_rng(9)
     act = synth.bf16_bits((rng.standard_normal((8192, 2048)) * 2).astype(np.float32))
@@ -394,6 +427,23 @@ def test_layer_full_size_end_to_end(L):
     assert np.array_equal(plan.row_src.cpu().numpy(), r.row_src)
     assert np.array_equal(plan.xq.q.cpu().numpy(), r.xq.q) and np.array_equal(plan.xq.sf.cpu().numpy(), r.xq.sf)
     check_bf16(got, r.out64, f"layer {L.name} out")
+
+
+@pytest.mark.timeout(600)
+def test_layer_decode_fused_static_scale_end_to_end():
+    """The decode layer with the SwiGLU output requantised in the gate/up GEMM's epilogue under
+    a static global scale (calibrated from the oracle's dynamic scale of the same act), against
+    the oracle layer with that static scale."""
+    L = synth.LAYER_DECODE
+    W1, W2, d1, d2 = layer_weights(L)
+    logits, x = synth.router_logits(L), synth.layer_activations(L)
+    r_dyn = oracle.moe_layer(logits, x, W1, W2, L.k)
+    g2 = float(r_dyn.actq.g)
+    plan = moe.MoELayerPlan(L.T, L.E, L.k, L.H, L.I, d1, d2, static_g2=dev(np.array([g2], np.float32)))
+    got = host_bits(plan.forward(dev(logits), dev_bf16(x)))
+    torch.cuda.synchronize()
+    r = oracle.moe_layer(logits, x, W1, W2, L.k, act_g=g2)
+    check_bf16(got, r.out64, "layer decode, fused static-scale requantisation")
 
 
 @pytest.mark.timeout(600)
