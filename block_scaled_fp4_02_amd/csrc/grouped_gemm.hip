@@ -12,8 +12,8 @@
 // Design (not the pages' SM120 tiles; this is for gfx950):
 //  * Work list: items (expert, row chunk, n tile), ordered expert-major, then n tile, then
 //    chunk.  Up to 64 experts every wave derives its own item from expert_offsets (a
-//    wave-wide sum and scan, no extra launch); above that a one-workgroup schedule kernel
-//    writes the list first.  The grid is the host-side upper bound on the
+//    wave-wide sum and scan, no extra launch); above that a schedule kernel writes the list
+//    first (each of its workgroups scans the offsets and writes a slice of the items).  The grid is the host-side upper bound on the
 //    item count; items past the device-side count exit.
 //  * Per-shape plan (the counterpart of the pages' tile table, chosen from host-known sizes
 //    only, so a supported launch cannot fail on its configuration):
@@ -32,10 +32,10 @@ namespace {
 
 // ---- work list ---------------------------------------------------------------
 
-// One workgroup: per block of 1024 experts, chunk counts, an inclusive scan of the item
-// counts (wave scans plus a scan of the 16 wave totals), then every thread writes items
-// w = t, t + 1024, ... of the block, finding each item's expert by binary search over the
-// scan.  Item counts stay below 2^31 (the grid bound is checked on the host).
+// A grid of workgroups: each computes, per block of 1024 experts, the chunk counts and an
+// inclusive scan of the item counts (wave scans plus a scan of the 16 wave totals), then
+// writes its slice of the block's items, finding each item's expert by binary search over
+// the scan.  Item counts stay below 2^31 (the grid bound is checked on the host).
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restrict__ offsets, int E,
                                                         int64_t R, int chunk_rows, int n_tiles, int64_t max_items,
                                                         int4 *__restrict__ items,
@@ -43,8 +43,10 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
   __shared__ int incl[1024];     // inclusive scan of the block's per-expert item counts
   __shared__ int first_row[1024];
   __shared__ int n_rows[1024];
+  __shared__ int n_chunks[1024];
   __shared__ int wave_total[16];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int G = static_cast<int>(gridDim.x), gi = static_cast<int>(blockIdx.x);
   int carry = 0;
   for (int base = 0; base < E; base += 1024) {
     const int e = base + t;
@@ -57,8 +59,8 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
       lo = static_cast<int>(l);
       rows = static_cast<int>(h - l);
     }
-    const int mine = (rows + chunk_rows - 1) / chunk_rows * n_tiles;
-    int v = mine;
+    const int chunks = (rows + chunk_rows - 1) / chunk_rows;
+    int v = chunks * n_tiles;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int u = __shfl_up(v, o, kWave);
@@ -71,25 +73,28 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
     incl[t] = before + v;
     first_row[t] = lo;
     n_rows[t] = rows;
+    n_chunks[t] = chunks;
     __syncthreads();
     const int block_items = incl[1023];
-    for (int w = t; w < block_items && carry + w < max_items; w += 1024) {
+    const int per = (block_items + G - 1) / G;   // this workgroup's slice of the block
+    const int w_end = block_items < (gi + 1) * per ? block_items : (gi + 1) * per;
+    for (int w = gi * per + t; w < w_end && carry + w < max_items; w += 1024) {
       int a = 0, b = 1023;   // first expert slot with incl > w
       while (a < b) {
         const int m = (a + b) >> 1;
         if (incl[m] > w) b = m;
         else a = m + 1;
       }
-      const int chunks = (n_rows[a] + chunk_rows - 1) / chunk_rows;
-      const int local = w - (incl[a] - chunks * n_tiles);
-      const int nt = local / chunks, c = local % chunks;
+      const int ch = n_chunks[a];
+      const int local = w - (incl[a] - ch * n_tiles);
+      const int nt = local / ch, c = local - nt * ch;
       const int nr = n_rows[a] - c * chunk_rows;
       items[carry + w] = make_int4(base + a, first_row[a] + c * chunk_rows, nr < chunk_rows ? nr : chunk_rows, nt);
     }
     carry += block_items;
     __syncthreads();
   }
-  if (t == 0) *count = static_cast<int>(carry < max_items ? carry : max_items);
+  if (gi == 0 && t == 0) *count = static_cast<int>(carry < max_items ? carry : max_items);
 }
 
 // ---- the packed weight layout ---------------------------------------------------
@@ -185,8 +190,10 @@ hipError_t launch_grouped_gemm(const moe_gemm_args &a, const GemmPlan &plan, voi
   int4 *items = nullptr;
   if (!plan.inline_schedule) {
     items = reinterpret_cast<int4 *>(static_cast<char *>(ws) + 16);
-    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, stream, a.expert_offsets, a.E, a.R,
-                       plan.chunk_rows, plan.n_tiles, plan.max_items, items, count);
+    // about 2048 items per workgroup (each repeats the cheap scan), at most 128 workgroups
+    const int64_t g = std::min<int64_t>(128, std::max<int64_t>(1, (plan.max_items + 2047) / 2048));
+    hipLaunchKernelGGL(schedule_kernel, dim3(static_cast<uint32_t>(g)), dim3(1024), 0, stream, a.expert_offsets,
+                       a.E, a.R, plan.chunk_rows, plan.n_tiles, plan.max_items, items, count);
   }
   const Params p{a.A, a.A_sf, a.A_gs, a.A_rows, a.rows_A, a.B, a.B_sf, a.B_gs, a.E, a.N, a.K,
                  a.D, a.amax_out, items, count, a.expert_offsets, a.R, plan.chunk_rows, plan.n_tiles,

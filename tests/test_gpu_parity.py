@@ -209,6 +209,7 @@ def _run_gemm_none(A, Bs, off, A_rows, R, label, packed=False):
     ([40, 0, 3], 1536, 256, False),                       # K split 2 ways inside a workgroup
     ([7, 25], 1024, 512, False),                          # K split 4 ways
     ([45, 3], 2048, 256, True),                           # K split 8 ways, 32 + 13 row chunks
+    ([0, 1, 2, 3, 5, 8, 13] * 150 + [40, 0], 256, 256, True),  # 1052 experts: two scan blocks in the schedule
     ([0, 0, 0], 256, 256, False),                         # no rows at all
     ([300], 256, 768, True),                              # one big group: several row chunks
     ([33] * 250 + [0, 64, 5] + [20] * 10, 256, 1024, True),  # enough groups for 4 tiles per wave
