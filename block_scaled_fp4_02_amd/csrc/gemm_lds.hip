@@ -32,17 +32,17 @@ namespace moe {
 namespace gemm {
 namespace {
 
-template <int MAXT>
+template <int MAXT, int WAVES>
 struct LdsShared {
   uint4 a[2][MAXT][8][64];   // [buffer][token tile][MFMA of step][lane]
-  float wmax[4];
+  float wmax[WAVES];
 };
 
-template <int NM, int EPI, int MAXT>
-__device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT> &sh, int b, int e, int row0, int nrows,
+template <int NM, int EPI, int MAXT, int WAVES>
+__device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES> &sh, int b, int e, int row0, int nrows,
                                          int nt) {
-  constexpr int SPAN = 256;                 // weight rows per workgroup (4 waves x 64)
-  constexpr int TPW = (MAXT + 3) / 4;       // token tiles a wave dequantises per step
+  constexpr int SPAN = 64 * WAVES;                  // weight rows per workgroup
+  constexpr int TPW = (MAXT + WAVES - 1) / WAVES;   // token tiles a wave dequantises per step
   static_assert(NM <= MAXT, "token tiles exceed the LDS buffer");
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -70,7 +70,7 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT> &sh, i
     b_scale[j] = static_cast<uint32_t>(nrow[j] / 16) * steps * kPackBlock + 2048 + lane * 4;
   }
 
-  // token tiles wv + 4i this wave dequantises (wave-uniform validity)
+  // token tiles wv + WAVES * i this wave dequantises (wave-uniform validity)
   const uint32_t half_k = P.K / 2, k16 = P.K / 16;
   const BufRsrc ra_codes = make_rsrc(P.A, static_cast<uint32_t>(P.rows_A * half_k));
   const BufRsrc ra_scales = make_rsrc(P.A_sf, static_cast<uint32_t>(P.rows_A * k16));
@@ -78,7 +78,7 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT> &sh, i
   uint32_t a_code[TPW], a_scale[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; i++) {
-    const int t = wv + 4 * i;
+    const int t = wv + WAVES * i;
     a_tile[i] = t < NM;
     a_code[i] = a_scale[i] = 0;
     if (a_tile[i]) {
@@ -108,7 +108,7 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT> &sh, i
 #pragma unroll
         for (int d = 0; d < 4; d++) {
           const half8 v = dequant8(word(f[i].q[q], d), sc[d >> 1]);
-          sh.a[buf][wv + 4 * i][4 * q + d][lane] = __builtin_bit_cast(uint4, v);
+          sh.a[buf][wv + WAVES * i][4 * q + d][lane] = __builtin_bit_cast(uint4, v);
         }
       }
     }
@@ -220,13 +220,17 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT> &sh, i
     amax = wave_max(amax);
     if (lane == 0) sh.wmax[wv] = amax;
     __syncthreads();
-    if (threadIdx.x == 0) P.amax_out[b] = fmaxf(fmaxf(sh.wmax[0], sh.wmax[1]), fmaxf(sh.wmax[2], sh.wmax[3]));
+    if (threadIdx.x == 0) {
+      float m = sh.wmax[0];
+      for (int w = 1; w < WAVES; w++) m = fmaxf(m, sh.wmax[w]);
+      P.amax_out[b] = m;
+    }
   }
 }
 
 template <int EPI>
 __global__ __launch_bounds__(256, 3) void gemm_lds_kernel(Params P) {
-  __shared__ LdsShared<kChunkTiles> sh;
+  __shared__ LdsShared<kChunkTiles, 4> sh;
   const int b = blockIdx.x;
   int4 item;
   if (!item_for_block(P, b, item)) {
@@ -239,6 +243,25 @@ __global__ __launch_bounds__(256, 3) void gemm_lds_kernel(Params P) {
   else lds_body<3, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
 }
 
+// Hundreds of rows per expert: eight waves share one activation tile of up to six token
+// tiles (96 rows), so each dequantised weight element serves twice as many tokens as in
+// gemm_lds_kernel, while two waves per SIMD (one workgroup of 512 threads per CU, 96 KB of
+// LDS) keep VALU and MFMA issuing side by side.  Token tiles rounded up to an even count.
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_lds_wide_kernel(Params P) {
+  __shared__ LdsShared<kWideChunkTiles, 8> sh;
+  const int b = blockIdx.x;
+  int4 item;
+  if (!item_for_block(P, b, item)) {
+    if (EPI == MOE_EPI_SWIGLU && threadIdx.x == 0) P.amax_out[b] = 0.f;
+    return;
+  }
+  const int nm = (item.z + 15) / 16;   // workgroup-uniform
+  if (nm <= 2) lds_body<2, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
+  else if (nm <= 4) lds_body<4, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
+  else lds_body<6, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
+}
+
 }  // namespace
 
 void launch_lds(const Params &p, int epi, dim3 grid, hipStream_t stream) {
@@ -247,6 +270,14 @@ void launch_lds(const Params &p, int epi, dim3 grid, hipStream_t stream) {
   else if (epi == MOE_EPI_SWIGLU_NVFP4)
     hipLaunchKernelGGL(gemm_lds_kernel<MOE_EPI_SWIGLU_NVFP4>, grid, block, 0, stream, p);
   else hipLaunchKernelGGL(gemm_lds_kernel<MOE_EPI_NONE>, grid, block, 0, stream, p);
+}
+
+void launch_lds_wide(const Params &p, int epi, dim3 grid, hipStream_t stream) {
+  const dim3 block(512);
+  if (epi == MOE_EPI_SWIGLU) hipLaunchKernelGGL(gemm_lds_wide_kernel<MOE_EPI_SWIGLU>, grid, block, 0, stream, p);
+  else if (epi == MOE_EPI_SWIGLU_NVFP4)
+    hipLaunchKernelGGL(gemm_lds_wide_kernel<MOE_EPI_SWIGLU_NVFP4>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(gemm_lds_wide_kernel<MOE_EPI_NONE>, grid, block, 0, stream, p);
 }
 
 }  // namespace gemm

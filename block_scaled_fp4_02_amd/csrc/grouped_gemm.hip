@@ -17,6 +17,7 @@
 //    item count; items past the device-side count exit.
 //  * Per-shape plan (the counterpart of the pages' tile table, chosen from host-known sizes
 //    only, so a supported launch cannot fail on its configuration):
+//      packed weights, >= 96 rows per expert       -> wide LDS kernel, 96-row chunks, 512-row n tiles
 //      packed weights, enough items for the chip   -> LDS kernel, 48-row chunks
 //      packed weights, few items (e.g. 8 groups)   -> K split 2/4/8 ways across a
 //                                                     workgroup's waves, 32-row chunks
@@ -151,7 +152,12 @@ GemmPlan plan_gemm(const moe_gemm_args &a) {
     p.chunk_rows = kChunkTiles * 16;
     p.ks = 1;
     p.n_tile = 256;
-    if (chunk_estimate(a, p.chunk_rows) * (a.N / 256) * 4 < kFullChip) {
+    if (a.R / a.E >= 96 && a.N % 512 == 0) {
+      // hundreds of rows per expert: the wide kernel (96-row chunks, 512 weight rows)
+      p.kernel = kLdsWide;
+      p.chunk_rows = kWideChunkTiles * 16;
+      p.n_tile = 512;
+    } else if (chunk_estimate(a, p.chunk_rows) * (a.N / 256) * 4 < kFullChip) {
       // few items: split K across the waves of a workgroup (2, 4 or 8 ways)
       const int chunk = ksplit_chunk_rows();
       for (int cand = 2; cand <= 8; cand *= 2) {
@@ -201,6 +207,7 @@ hipError_t launch_grouped_gemm(const moe_gemm_args &a, const GemmPlan &plan, voi
   const dim3 grid(static_cast<uint32_t>(plan.grid));
   switch (plan.kernel) {
     case kLds: launch_lds(p, a.epilogue, grid, stream); break;
+    case kLdsWide: launch_lds_wide(p, a.epilogue, grid, stream); break;
     case kKSplit: launch_ksplit(p, a.epilogue, plan.ks, grid, stream); break;
     default: launch_rowmajor(p, a.epilogue, plan.ks, grid, stream); break;
   }

@@ -217,6 +217,9 @@ def _run_gemm_none(A, Bs, off, A_rows, R, label, packed=False):
     # in the second case, an odd number of 256-wide K steps
     ([0, 1, 96, 127, 128, 129, 300, 513], 512, 512, True),
     ([100, 200, 57, 0], 768, 256, True),
+    # >= 96 rows per expert and N % 512 == 0: the 8-wave kernel with 96-row chunks; the groups
+    # end in every token-tile count 1..6
+    ([1, 17, 33, 49, 65, 81, 95, 96, 97, 200, 600], 512, 512, True),
 ])
 def test_gemm_none_shapes(sizes, K, N, gather, packed):
     A, Bs, off, A_rows, R = _gemm_case(sizes, K, N, gather, seed=sum(sizes) + K + N)
@@ -323,7 +326,8 @@ def test_gemm_swiglu_shapes(sizes, K, I, packed):
 
 @pytest.mark.parametrize("sizes,K,I,g_div", [([8, 6, 9, 9], 256, 256, 1.0), ([0, 17, 33, 64, 65, 1], 512, 384, 4.0),
                                              ([40] * 256 + [3, 0, 64], 256, 512, 1.0),   # LDS kernel
-                                             ([20, 32], 2048, 256, 1.0)])                # K split 8 ways
+                                             ([20, 32], 2048, 256, 1.0),                 # K split 8 ways
+                                             ([0, 130, 255, 97], 768, 256, 2.0)])        # 8-wave kernel
 def test_gemm_swiglu_nvfp4_fused(sizes, K, I, g_div):
     """SwiGLU + NVFP4 epilogue with a static global scale g2: codes and scales equal the
     oracle's static-scale quantisation of the GPU's own SwiGLU output byte for byte (same
