@@ -249,20 +249,26 @@ def run_layer(L, moe, torch, steps: int, warmup: int, weights=None, fused: bool 
         plan.forward(logits, x)
     torch.cuda.synchronize()
 
+    # stage breakdown: the six calls one after another on one stream, events between them
     stream = torch.cuda.current_stream()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(steps):
         evs[s][0].record(stream)
         for i, c in enumerate(calls):
             c()
             evs[s][i + 1].record(stream)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / steps
     stage_us = {st: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)]) * 1e3)
                 for i, st in enumerate(stages)}
+    # the timed steps: whole forward passes (routing and token quantisation overlap on two
+    # streams), bracketed by device synchronisation
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        plan.forward(logits, x)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
 
     off = plan.off.cpu().numpy()
     sizes = np.diff(off)

@@ -318,6 +318,9 @@ class MoELayerPlan:
         self.ws_q2 = _ws(L.moe_quantize_nvfp4_workspace(R, I), dev)
         self.ws_g1 = _ws(moe_grouped_gemm_nvfp4_workspace(self.args1), dev)
         self.ws_g2 = _ws(moe_grouped_gemm_nvfp4_workspace(self.args2), dev)
+        # routing reads the logits and the token quantiser reads x: independent, so forward()
+        # runs the quantiser on a second stream (default priority) beside the routing kernels
+        self.side = torch.cuda.Stream(device=dev)
 
     # the six calls of the layer, individually (the benchmark times them one by one)
     def route(self, logits, stream=None):
@@ -343,12 +346,15 @@ class MoELayerPlan:
         moe_finalize(self.Y, self.w, self.tsr, self.out, stream)
 
     def forward(self, logits, x, stream=None):
-        self.route(logits, stream)
-        self.quantize_input(x, stream)
-        self.gemm1(stream)
-        self.requantize(stream)
-        self.gemm2(stream)
-        self.finalize(stream)
+        main = stream if stream is not None else torch.cuda.current_stream()
+        self.side.wait_stream(main)          # logits and x are ready on the main stream
+        self.quantize_input(x, self.side)
+        self.route(logits, main)
+        main.wait_stream(self.side)          # GEMM1 needs both
+        self.gemm1(main)
+        self.requantize(main)
+        self.gemm2(main)
+        self.finalize(main)
         return self.out
 
 
