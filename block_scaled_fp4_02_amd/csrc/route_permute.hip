@@ -8,8 +8,8 @@
 //
 // Kernels (all integer work is exact, so the outputs are bit-identical run to run):
 //   topk_kernel        one wavefront per token: k rounds of a wave arg-max over the
-//                      token's logits (ties -> lower id), then the softmax of the k
-//                      winners in slot order.
+//                      token's logits (ties -> lower id; 64-bit keys reduced with DPP lane
+//                      moves), then the softmax of the k winners in slot order.
 //   chunk_count_kernel one workgroup per chunk of 256 tokens: a 256-bit token bitmap
 //                      per expert in LDS (order-free OR), popcounts -> counts[chunk][e].
 //   offsets_kernel     one workgroup: per expert an exclusive scan over chunks, then
@@ -20,7 +20,6 @@
 //                      each expert at most once.
 #include "common.hpp"
 
-#include <limits.h>
 
 namespace moe {
 namespace {
@@ -30,6 +29,50 @@ constexpr int kMaxPerLane = kMaxE / kWave;  // logits held per lane
 constexpr int kChunk = 256;                 // tokens per permutation chunk
 constexpr int kWords = kChunk / 64;         // 64-bit bitmap words per expert
 
+// A candidate (logit v, expert id) as one 64-bit key whose unsigned order is the selection
+// order: larger logit first, then lower id.  High word: the float's bits made monotone
+// (negative values inverted, positive ones with the sign bit set); low word: ~id.  Key 0
+// marks "no candidate" (every real key has a high word >= 0x007fffff).
+__device__ __forceinline__ uint64_t cand_key(float v, int id) {
+  const uint32_t b = __float_as_uint(v + 0.0f);   // -0 -> +0: equal logits must tie on the id
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (static_cast<uint64_t>(ord) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(id));
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t ord = static_cast<uint32_t>(key >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+
+__device__ __forceinline__ int key_id(uint64_t key) { return static_cast<int>(~static_cast<uint32_t>(key)); }
+
+// One DPP step of a wave max over 64-bit keys: take the partner lane's key (selected by
+// the DPP control; rows outside row_mask keep their own) if it is larger.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t k) {
+  const int lo = static_cast<int>(static_cast<uint32_t>(k));
+  const int hi = static_cast<int>(k >> 32);
+  const uint32_t plo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false));
+  const uint32_t phi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false));
+  const uint64_t p = (static_cast<uint64_t>(phi) << 32) | plo;
+  return p > k ? p : k;
+}
+
+// Maximum key over the wave, read from lane 63 (wave-uniform): pairs within quads, then
+// the two halves of each 8-lane group, the two halves of each 16-lane row, then the rows
+// through the row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  k = dpp_max_step<0xb1, 0xf>(k);    // quad_perm [1, 0, 3, 2]
+  k = dpp_max_step<0x4e, 0xf>(k);    // quad_perm [2, 3, 0, 1]
+  k = dpp_max_step<0x141, 0xf>(k);   // row_half_mirror
+  k = dpp_max_step<0x140, 0xf>(k);   // row_mirror
+  k = dpp_max_step<0x142, 0xa>(k);   // row_bcast15 into rows 1 and 3
+  k = dpp_max_step<0x143, 0xc>(k);   // row_bcast31 into rows 2 and 3
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(k)), 63));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(k >> 32), 63));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
                                                    int k, int32_t *__restrict__ topk_ids,
                                                    float *__restrict__ topk_w) {
@@ -37,45 +80,28 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float *L = logits + static_cast<int64_t>(t) * E;
-  float v[kMaxPerLane];
-  uint32_t absent = 0;  // bit i: element lane + 64 i is taken or does not exist
+  uint64_t key[kMaxPerLane];   // this lane's candidates: experts lane + 64 i (0: none / taken)
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; i++) {
     const int e = lane + kWave * i;
-    if (e < E) {
-      v[i] = L[e];
-    } else {
-      v[i] = 0.f;
-      absent |= 1u << i;
-    }
+    key[i] = e < E ? cand_key(L[e], e) : 0ull;
   }
   float my_v = 0.f;
   int my_id = 0;
   for (int j = 0; j < k; j++) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
+    uint64_t best = 0ull;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; i++) {
-      // ids grow with i, so a strictly larger value is needed to displace the best
-      if (!((absent >> i) & 1u) && (bi == INT_MAX || v[i] > bv)) {
-        bv = v[i];
-        bi = lane + kWave * i;
-      }
-    }
+    for (int i = 0; i < kMaxPerLane; i++) best = key[i] > best ? key[i] : best;
+    const uint64_t win = wave_max_key(best);
+    const int id = key_id(win);
+    if ((id & 63) == lane) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      const bool better = oi != INT_MAX && (bi == INT_MAX || ov > bv || (ov == bv && oi < bi));
-      if (better) {
-        bv = ov;
-        bi = oi;
-      }
+      for (int i = 0; i < kMaxPerLane; i++)
+        if (i == (id >> 6)) key[i] = 0ull;
     }
-    if ((bi & 63) == lane) absent |= 1u << (bi >> 6);
     if (lane == j) {
-      my_v = bv;
-      my_id = bi;
+      my_v = key_value(win);
+      my_id = id;
     }
   }
   const float v0 = __shfl(my_v, 0, kWave);
