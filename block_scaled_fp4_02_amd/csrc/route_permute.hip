@@ -12,9 +12,10 @@
 //                      moves), then the softmax of the k winners in slot order.
 //   chunk_count_kernel one workgroup per chunk of 256 tokens: a 256-bit token bitmap
 //                      per expert in LDS (order-free OR), popcounts -> counts[chunk][e].
-//   offsets_kernel     one workgroup: per expert an exclusive scan over chunks, then
-//                      an exclusive scan over experts -> expert_offsets.
-//   scatter_kernel     one workgroup per chunk: rebuild the bitmaps; the rank of token t
+//   scatter_kernel     one workgroup per chunk: from the chunk counts, the start of each
+//                      expert's rows in this chunk (column prefix over earlier chunks plus
+//                      an exclusive scan over experts; chunk 0 also writes expert_offsets);
+//                      then rebuild the bitmaps; the rank of token t
 //                      in expert e's group within the chunk is the popcount of the bits
 //                      below t, which is the stable order t*k + j because a token names
 //                      each expert at most once.
@@ -145,37 +146,61 @@ __global__ __launch_bounds__(kChunk) void chunk_count_kernel(const int32_t *__re
   }
 }
 
-__global__ __launch_bounds__(1024) void offsets_kernel(int32_t *__restrict__ counts, int nchunks,
-                                                       int E, int32_t *__restrict__ offsets) {
-  __shared__ int32_t s[1024];
-  const int e = threadIdx.x;
-  int total = 0;
-  if (e < E) {
-    for (int c = 0; c < nchunks; c++) {  // counts[c][e] becomes its exclusive prefix over chunks
-      const int64_t i = static_cast<int64_t>(c) * E + e;
-      const int n = counts[i];
-      counts[i] = total;
-      total += n;
+// Per workgroup (chunk c): base[e] = expert_offsets[e] + (rows of expert e in chunks < c),
+// from the read-only chunk counts -- a column sum per expert, then an exclusive scan over
+// experts.  Workgroup 0 also writes expert_offsets.
+__device__ __forceinline__ void chunk_bases(const int32_t *__restrict__ counts, int nchunks, int E, int chunk,
+                                            int32_t *base, int32_t *wave_total,
+                                            int32_t *__restrict__ offsets) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  constexpr int kPer = kMaxE / kChunk;   // experts per thread
+  int total[kPer], before[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; i++) {
+    const int e = t * kPer + i;   // consecutive experts per thread keep the scan simple
+    total[i] = before[i] = 0;
+    if (e < E) {
+      for (int c = 0; c < nchunks; c++) {
+        const int n = counts[static_cast<int64_t>(c) * E + e];
+        total[i] += n;
+        if (c < chunk) before[i] += n;
+      }
     }
+    mine += total[i];
   }
-  s[e] = total;
+  int v = mine;   // inclusive scan of per-thread totals: wave scan, then the 4 wave totals
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wave_total[wv] = v;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan over experts
-    const int add = (e >= o) ? s[e - o] : 0;
-    __syncthreads();
-    s[e] += add;
-    __syncthreads();
+  int excl = v - mine;
+  for (int w = 0; w < wv; w++) excl += wave_total[w];
+#pragma unroll
+  for (int i = 0; i < kPer; i++) {
+    const int e = t * kPer + i;
+    if (e < E) {
+      base[e] = excl + before[i];
+      if (chunk == 0) offsets[e] = excl;
+      if (chunk == 0 && e == E - 1) offsets[E] = excl + total[i];
+    }
+    excl += total[i];
   }
-  if (e < E) offsets[e] = s[e] - total;
-  if (e == E - 1) offsets[E] = s[e];
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(kChunk) void scatter_kernel(const int32_t *__restrict__ ids, int T, int E,
-                                                         int k, const int32_t *__restrict__ counts,
-                                                         const int32_t *__restrict__ offsets,
+                                                         int k, const int32_t *__restrict__ counts, int nchunks,
+                                                         int32_t *__restrict__ offsets,
                                                          int32_t *__restrict__ row_src,
                                                          int32_t *__restrict__ token_slot_row) {
   __shared__ unsigned long long bm[kMaxE * kWords];
+  __shared__ int32_t base[kMaxE];
+  __shared__ int32_t wave_total[kChunk / 64];
+  chunk_bases(counts, nchunks, E, blockIdx.x, base, wave_total, offsets);
   build_bitmaps(bm, ids, T, E, k, blockIdx.x);
   const int t = blockIdx.x * kChunk + threadIdx.x;
   if (t >= T) return;
@@ -186,11 +211,16 @@ __global__ __launch_bounds__(kChunk) void scatter_kernel(const int32_t *__restri
     const int e = clamp_expert(ids[static_cast<int64_t>(t) * k + j], E);
     int rank = __popcll(bm[e * kWords + word] & below);
     for (int w = 0; w < word; w++) rank += __popcll(bm[e * kWords + w]);
-    int64_t p = static_cast<int64_t>(offsets[e]) + counts[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
+    int64_t p = static_cast<int64_t>(base[e]) + rank;
     p = p < 0 ? 0 : (p >= n ? n - 1 : p);
     row_src[p] = t;
     token_slot_row[static_cast<int64_t>(t) * k + j] = static_cast<int32_t>(p);
   }
+}
+
+// No tokens: every group is empty.
+__global__ __launch_bounds__(kMaxE) void zero_offsets_kernel(int E, int32_t *__restrict__ offsets) {
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = 0;
 }
 
 }  // namespace
@@ -210,12 +240,10 @@ hipError_t launch_route_permute(const float *logits, int T, int E, int k, int32_
                        topk_ids, topk_w);
     hipLaunchKernelGGL(chunk_count_kernel, dim3(nchunks), dim3(kChunk), 0, stream, topk_ids, T, E,
                        k, counts);
-  }
-  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, stream, counts, nchunks, E,
-                     expert_offsets);
-  if (T > 0) {
     hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(kChunk), 0, stream, topk_ids, T, E, k,
-                       counts, expert_offsets, row_src, token_slot_row);
+                       counts, nchunks, expert_offsets, row_src, token_slot_row);
+  } else {
+    hipLaunchKernelGGL(zero_offsets_kernel, dim3(1), dim3(kMaxE), 0, stream, E, expert_offsets);
   }
   return hipGetLastError();
 }
