@@ -38,7 +38,8 @@
  *  - Every data pointer is a DEVICE pointer on the current HIP device, owned by
  *    the caller; the library allocates no device memory, keeps no pointer after
  *    it returns and holds no global state apart from a thread-local last HIP
- *    error code.
+ *    error code.  Tensor base pointers are 16-byte aligned (as every device
+ *    allocation is) and tensors are dense, row-major.
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream); no call
  *    synchronises with the device or copies device data to the host.
  *  - Arguments are validated on the host before any HIP call; failures return a
