@@ -34,29 +34,58 @@ __device__ __forceinline__ float load_abs_max8_bf16(const uint4 v) {
   return m;
 }
 
-__global__ __launch_bounds__(256) void amax_kernel(const void *__restrict__ x, int x_dtype, int64_t n,
-                                                   const float *__restrict__ amax_in, int64_t n_in,
-                                                   float *__restrict__ parts) {
+// Partial maxima, one per workgroup of kAmaxThreads.  Each thread takes kAmaxBatch grid-strided
+// loads per round and issues them all before using any (a maximum does not mind an element
+// read twice, so indices past the end are clamped to the last one instead of branched
+// around): enough bytes in flight to stream HBM with at most kAmaxParts workgroups.
+constexpr int kAmaxThreads = 1024;
+constexpr int kAmaxBatch = 4;
+
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const void *__restrict__ x, int x_dtype, int64_t n,
+                                                            const float *__restrict__ amax_in, int64_t n_in,
+                                                            float *__restrict__ parts) {
   float m = 0.f;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (amax_in != nullptr) {
-    for (int64_t i = tid; i < n_in; i += stride) m = fmaxf(m, fabsf(amax_in[i]));
+    for (int64_t i = tid; i < n_in; i += kAmaxBatch * stride) {
+      float v[kAmaxBatch];
+#pragma unroll
+      for (int u = 0; u < kAmaxBatch; u++) v[u] = amax_in[min(i + u * stride, n_in - 1)];
+#pragma unroll
+      for (int u = 0; u < kAmaxBatch; u++) m = fmaxf(m, fabsf(v[u]));
+    }
   } else if (x_dtype == MOE_DTYPE_BF16) {
     const uint4 *xv = static_cast<const uint4 *>(x);  // 8 bf16 per load; n % 16 == 0
-    for (int64_t i = tid; i < n / 8; i += stride) m = fmaxf(m, load_abs_max8_bf16(xv[i]));
+    const int64_t nv = n / 8;
+    for (int64_t i = tid; i < nv; i += kAmaxBatch * stride) {
+      uint4 v[kAmaxBatch];
+#pragma unroll
+      for (int u = 0; u < kAmaxBatch; u++) v[u] = xv[min(i + u * stride, nv - 1)];
+#pragma unroll
+      for (int u = 0; u < kAmaxBatch; u++) m = fmaxf(m, load_abs_max8_bf16(v[u]));
+    }
   } else {
     const float4 *xv = static_cast<const float4 *>(x);
-    for (int64_t i = tid; i < n / 4; i += stride) {
-      const float4 v = xv[i];
-      m = fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+    const int64_t nv = n / 4;
+    for (int64_t i = tid; i < nv; i += kAmaxBatch * stride) {
+      float4 v[kAmaxBatch];
+#pragma unroll
+      for (int u = 0; u < kAmaxBatch; u++) v[u] = xv[min(i + u * stride, nv - 1)];
+#pragma unroll
+      for (int u = 0; u < kAmaxBatch; u++)
+        m = fmaxf(fmaxf(m, fmaxf(fabsf(v[u].x), fabsf(v[u].y))), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
     }
   }
   m = wave_max(m);
-  __shared__ float wm[4];
+  __shared__ float wm[kAmaxThreads / 64];
   if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) parts[blockIdx.x] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  if (threadIdx.x == 0) {
+    float r = wm[0];
+    for (int w = 1; w < kAmaxThreads / 64; w++) r = fmaxf(r, wm[w]);
+    parts[blockIdx.x] = r;
+  }
 }
 
 __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, int x_dtype,
@@ -68,8 +97,13 @@ __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, 
   if (threadIdx.x < 64) {
     float g;
     if (dynamic) {
-      float m = 0.f;
-      for (int i = threadIdx.x; i < nparts; i += 64) m = fmaxf(m, parts[i]);
+      // nparts <= kAmaxParts = 4 * 64: four loads per lane, all in flight at once (indices
+      // clamped to the last partial, which a maximum may read twice)
+      static_assert(kAmaxParts <= 4 * 64, "one round of loads covers the partial maxima");
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) v[u] = parts[min(static_cast<int>(threadIdx.x) + 64 * u, nparts - 1)];
+      float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
       m = wave_max(m);
       g = (m > 0.f) ? m / 2688.0f : 1.0f;  // 2688 = 6 * 448
       if (blockIdx.x == 0 && threadIdx.x == 0) *gs = g;
@@ -114,7 +148,10 @@ __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, 
 #pragma unroll
   for (int i = 0; i < 16; i++) {
     const uint32_t sign = (__float_as_uint(v[i]) >> 31) << 3;
-    const uint32_t mag = (s != 0u) ? e2m1_rne(fminf(fabsf(v[i]) / sg, 6.0f)) : 0u;
+    // computed for every block and discarded when s = 0 (then sg = 0 and the quotient is
+    // inf or NaN; fminf returns 6 for NaN): no branch per element
+    const uint32_t code = e2m1_rne(fminf(fabsf(v[i]) / sg, 6.0f));
+    const uint32_t mag = (s != 0u) ? code : 0u;
     packed[i >> 3] |= (sign | mag) << (4 * (i & 7));
   }
   reinterpret_cast<uint2 *>(q)[b] = make_uint2(packed[0], packed[1]);
@@ -135,9 +172,10 @@ hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t C, 
   int nparts = 0;
   if (dynamic) {
     // partial maxima: ~4 per thread; tensor data: ~32 elements per thread
-    const int64_t g = amax_in ? (n_amax_in + 1023) / 1024 : (n + 256 * 32 - 1) / (256 * 32);
+    const int64_t per_wg = kAmaxThreads * (amax_in ? 4 : 32);
+    const int64_t g = ((amax_in ? n_amax_in : n) + per_wg - 1) / per_wg;
     nparts = static_cast<int>(g < 1 ? 1 : (g > kAmaxParts ? kAmaxParts : g));
-    hipLaunchKernelGGL(amax_kernel, dim3(nparts), dim3(256), 0, stream, x, x_dtype, n, amax_in,
+    hipLaunchKernelGGL(amax_kernel, dim3(nparts), dim3(kAmaxThreads), 0, stream, x, x_dtype, n, amax_in,
                        n_amax_in, parts);
   }
   if (nblk > 0 || dynamic) {

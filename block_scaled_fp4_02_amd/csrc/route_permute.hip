@@ -9,7 +9,8 @@
 // Kernels (all integer work is exact, so the outputs are bit-identical run to run):
 //   topk_kernel        one wavefront per token: k rounds of a wave arg-max over the
 //                      token's logits (ties -> lower id; 64-bit keys reduced with DPP lane
-//                      moves), then the softmax of the k winners in slot order.
+//                      moves), then the softmax of the k winners in slot order.  Sized by
+//                      the expert count (1..16 logits per lane).
 //   chunk_count_kernel one workgroup per chunk of 256 tokens: a 256-bit token bitmap
 //                      per expert in LDS (order-free OR), popcounts -> counts[chunk][e].
 //   scatter_kernel     one workgroup per chunk: from the chunk counts, the start of each
@@ -74,6 +75,10 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// PER = logits per lane (E <= 64 PER).  All of a lane's logit loads are issued before any is
+// used (an out-of-range lane reads the token's last logit and discards it), so they share one
+// memory latency instead of waiting in turn behind a branch each.
+template <int PER>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
                                                    int k, int32_t *__restrict__ topk_ids,
                                                    float *__restrict__ topk_w) {
@@ -81,23 +86,29 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float *L = logits + static_cast<int64_t>(t) * E;
-  uint64_t key[kMaxPerLane];   // this lane's candidates: experts lane + 64 i (0: none / taken)
+  float lv[PER];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; i++) {
+  for (int i = 0; i < PER; i++) {
     const int e = lane + kWave * i;
-    key[i] = e < E ? cand_key(L[e], e) : 0ull;
+    lv[i] = L[e < E ? e : E - 1];
+  }
+  uint64_t key[PER];   // this lane's candidates: experts lane + 64 i (0: none / taken)
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    const int e = lane + kWave * i;
+    key[i] = e < E ? cand_key(lv[i], e) : 0ull;
   }
   float my_v = 0.f;
   int my_id = 0;
   for (int j = 0; j < k; j++) {
     uint64_t best = 0ull;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; i++) best = key[i] > best ? key[i] : best;
+    for (int i = 0; i < PER; i++) best = key[i] > best ? key[i] : best;
     const uint64_t win = wave_max_key(best);
     const int id = key_id(win);
     if ((id & 63) == lane) {
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; i++)
+      for (int i = 0; i < PER; i++)
         if (i == (id >> 6)) key[i] = 0ull;
     }
     if (lane == j) {
@@ -154,19 +165,34 @@ __device__ __forceinline__ void chunk_bases(const int32_t *__restrict__ counts, 
                                             int32_t *__restrict__ offsets) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   constexpr int kPer = kMaxE / kChunk;   // experts per thread
+  constexpr int kBatch = 8;              // chunks whose counts are loaded together
   int total[kPer], before[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; i++) total[i] = before[i] = 0;
+  // consecutive experts per thread keep the scan simple; every load of a batch is issued
+  // before any is summed (indices clamped into the table, out-of-range terms dropped)
+  for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+    int n[kPer][kBatch];
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      const int e = min(t * kPer + i, E - 1);
+#pragma unroll
+      for (int u = 0; u < kBatch; u++)
+        n[i][u] = counts[static_cast<int64_t>(min(c0 + u, nchunks - 1)) * E + e];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; i++)
+#pragma unroll
+      for (int u = 0; u < kBatch; u++) {
+        const int c = c0 + u;
+        total[i] += c < nchunks ? n[i][u] : 0;
+        before[i] += c < chunk ? n[i][u] : 0;
+      }
+  }
   int mine = 0;
 #pragma unroll
   for (int i = 0; i < kPer; i++) {
-    const int e = t * kPer + i;   // consecutive experts per thread keep the scan simple
-    total[i] = before[i] = 0;
-    if (e < E) {
-      for (int c = 0; c < nchunks; c++) {
-        const int n = counts[static_cast<int64_t>(c) * E + e];
-        total[i] += n;
-        if (c < chunk) before[i] += n;
-      }
-    }
+    if (t * kPer + i >= E) total[i] = before[i] = 0;
     mine += total[i];
   }
   int v = mine;   // inclusive scan of per-thread totals: wave scan, then the 4 wave totals
@@ -236,8 +262,12 @@ hipError_t launch_route_permute(const float *logits, int T, int E, int k, int32_
   int32_t *counts = static_cast<int32_t *>(ws);
   const int nchunks = (T + kChunk - 1) / kChunk;
   if (T > 0) {
-    hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k,
-                       topk_ids, topk_w);
+    const dim3 tg((T + 3) / 4), tb(256);
+    if (E <= 64) hipLaunchKernelGGL(topk_kernel<1>, tg, tb, 0, stream, logits, T, E, k, topk_ids, topk_w);
+    else if (E <= 128) hipLaunchKernelGGL(topk_kernel<2>, tg, tb, 0, stream, logits, T, E, k, topk_ids, topk_w);
+    else if (E <= 256) hipLaunchKernelGGL(topk_kernel<4>, tg, tb, 0, stream, logits, T, E, k, topk_ids, topk_w);
+    else if (E <= 512) hipLaunchKernelGGL(topk_kernel<8>, tg, tb, 0, stream, logits, T, E, k, topk_ids, topk_w);
+    else hipLaunchKernelGGL(topk_kernel<kMaxPerLane>, tg, tb, 0, stream, logits, T, E, k, topk_ids, topk_w);
     hipLaunchKernelGGL(chunk_count_kernel, dim3(nchunks), dim3(kChunk), 0, stream, topk_ids, T, E,
                        k, counts);
     hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(kChunk), 0, stream, topk_ids, T, E, k,
