@@ -25,13 +25,11 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 // E2M1 magnitude code for u in [0, 6], ties to the even code.  Below 1 the E2M1 values are
 // the multiples of 0.5 (code = 2u rounded to nearest even); from 1 up they have one mantissa
 // bit, so the binary32 mantissa is rounded to one bit and the exponent rebiased (127 -> 1).
-// Both candidates are computed and one selected: no divergent branch per element.
 __device__ __forceinline__ uint32_t e2m1_rne(float u) {
-  const uint32_t below_one = static_cast<uint32_t>(rintf(u * 2.0f));
+  if (u < 1.0f) return static_cast<uint32_t>(rintf(u * 2.0f));
   uint32_t b = __float_as_uint(u);
   b += 0x1fffffu + ((b >> 22) & 1u);
-  const uint32_t from_one = (b >> 22) - (126u << 1);
-  return u < 1.0f ? below_one : from_one;
+  return (b >> 22) - (126u << 1);
 }
 
 }  // namespace moe

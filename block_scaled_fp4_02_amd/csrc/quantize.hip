@@ -148,10 +148,7 @@ __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, 
 #pragma unroll
   for (int i = 0; i < 16; i++) {
     const uint32_t sign = (__float_as_uint(v[i]) >> 31) << 3;
-    // computed for every block and discarded when s = 0 (then sg = 0 and the quotient is
-    // inf or NaN; fminf returns 6 for NaN): no branch per element
-    const uint32_t code = e2m1_rne(fminf(fabsf(v[i]) / sg, 6.0f));
-    const uint32_t mag = (s != 0u) ? code : 0u;
+    const uint32_t mag = (s != 0u) ? e2m1_rne(fminf(fabsf(v[i]) / sg, 6.0f)) : 0u;
     packed[i >> 3] |= (sign | mag) << (4 * (i & 7));
   }
   reinterpret_cast<uint2 *>(q)[b] = make_uint2(packed[0], packed[1]);
