@@ -125,17 +125,22 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
 #pragma unroll
     for (int mt = 0; mt < NM; mt++) acc[j][mt] = float4v{};
 
-  // Loads are issued in the same order in the prologue as in every step: the weights of a
-  // step, then the activation tiles of the step after it.
+  // Each step first writes the activation tiles of the next step into the other LDS buffer
+  // (every wave finished reading it before the last barrier), loads the tiles of the step
+  // after that and the next step's weights, then runs its MFMAs: a writer wave whose weights
+  // are still in flight spends the wait on activation work.  The prologue issues the same
+  // loads in the same order.
   Frag16 f0[4], f1[4], ra[TPW], ra0[TPW];
-  load_b(f0, 0);
   load_a(ra0, 0);
   load_a(ra, 1);
+  load_b(f0, 0);
   store_a(ra0, 0);
   __syncthreads();
 
   auto step = [&](const Frag16 (&fb)[4], Frag16 (&fl)[4], int s) {
     const int buf = s & 1;
+    if (s + 1 < steps) store_a(ra, buf ^ 1);   // activation tiles of step s + 1
+    load_a(ra, s + 2);
     load_b(fl, s + 1);
 #pragma unroll
     for (int q = 0; q < 2; q++) {
@@ -156,8 +161,6 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
         }
       }
     }
-    if (s + 1 < steps) store_a(ra, buf ^ 1);   // activation tiles of step s + 1
-    load_a(ra, s + 2);
     __syncthreads();
   };
   int s = 0;
