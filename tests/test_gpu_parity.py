@@ -313,7 +313,7 @@ def _run_gemm_swiglu(A, Bs, off, A_rows, R, label, rows=None, packed=False):
     print(f"  act: max diff {diff.max():.3e}, max bound-ratio {(diff / bound).max():.3f}, "
           f"exact {(got_all[rows] == oracle.swiglu(y1)).mean():.5f}", flush=True)
     assert (diff <= bound).all()
-    check_bf16(got_all[rows], ref, f"gemm SWIGLU {label} (north-star bar)")
+    check_bf16(got_all[rows], ref, f"gemm SWIGLU {label} (bf16 output bar)")
 
 
 @pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
