@@ -136,3 +136,42 @@ def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(moe, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         moe.lib()
+
+
+def test_header_is_c11_and_matches_the_binding(tmp_path):
+    """include/moe_nvfp4.h compiles as C11 with warnings as errors, and the binding's view of
+    it agrees: the size and every field offset of moe_gemm_args, and every enum constant."""
+    import ctypes
+    import shutil
+    import subprocess
+
+    import block_scaled_fp4_02_amd as m
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    fields = [f for f, _ in m.moe_gemm_args._fields_]
+    consts = ["MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
+              "MOE_ERR_HIP", "MOE_DTYPE_BF16", "MOE_DTYPE_F32", "MOE_GS_STATIC", "MOE_GS_DYNAMIC",
+              "MOE_EPI_NONE", "MOE_EPI_SWIGLU", "MOE_EPI_SWIGLU_NVFP4", "MOE_LAYOUT_ROWMAJOR",
+              "MOE_LAYOUT_PACKED"]
+    src = ["#include <stdio.h>", "#include <stddef.h>", '#include "moe_nvfp4.h"', "int main(void) {",
+           '  printf("size %zu\\n", sizeof(moe_gemm_args));']
+    src += [f'  printf("off {f} %zu\\n", offsetof(moe_gemm_args, {f}));' for f in fields]
+    src += [f'  printf("const {c} %d\\n", (int){c});' for c in consts]
+    src += ["  return 0;", "}"]
+    (tmp_path / "abi.c").write_text("\n".join(src) + "\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = tmp_path / "abi"
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(root, "include"), "-I", "/opt/rocm/include",
+                    str(tmp_path / "abi.c"), "-o", str(exe)], check=True)
+    got = {}
+    for ln in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        *key, value = ln.split()
+        got[" ".join(key)] = int(value)
+    assert got["size"] == ctypes.sizeof(m.moe_gemm_args)
+    for f in fields:
+        assert got[f"off {f}"] == getattr(m.moe_gemm_args, f).offset, f
+    for c in consts:
+        assert got[f"const {c}"] == getattr(m, c), c
