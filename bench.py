@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times (to scale HBM "
                          "byte counters against a kernel of known traffic) and exit")
+    ap.add_argument("--power-sample", action="store_true",
+                    help="only run the decode layer's GEMMs back to back for a few seconds each while "
+                         "amd-smi samples board power and clocks midway; print one JSON line and exit")
     return ap.parse_args()
 
 
@@ -80,6 +83,60 @@ def copy_calibration(mib: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def copy_bandwidth(torch, mib: int = 2048, launches: int = 10) -> float:
+    """Bytes moved per second (read + write) by a plain device-to-device copy of `mib` MiB:
+    the streaming rate the machine's HBM reaches on this image, a measured companion to the
+    8 TB/s spec peak."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(launches):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2.0 * n * launches / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
+
+
+def power_sample(moe, torch):
+    """Decode layer: each grouped GEMM launched back to back for ~5 s while `amd-smi metric`
+    (a child process) samples socket power and clocks once, 2 s in."""
+    import subprocess
+    import synth
+    L = synth.LAYER_DECODE
+    W1, W2 = make_weights(L, moe, torch)
+    logits = torch.from_numpy(synth.router_logits(L)).cuda()
+    x = torch.from_numpy(synth.layer_activations(L).view(np.int16)).cuda().view(torch.bfloat16)
+    plan = moe.MoELayerPlan(L.T, L.E, L.k, L.H, L.I, W1, W2)
+    plan.forward(logits, x)
+    torch.cuda.synchronize()
+    out = {"workload": L.name}
+    for tag, fn in (("gemm1", plan.gemm1), ("gemm2", plan.gemm2)):
+        t0, n, proc = time.time(), 0, None
+        while time.time() - t0 < 5:
+            for _ in range(20):
+                fn()
+            n += 20
+            if proc is None and time.time() - t0 > 2:
+                proc = subprocess.Popen(["amd-smi", "metric", "-p", "-c", "-g", "0", "--json"],
+                                        stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+        torch.cuda.synchronize()
+        rec = {"avg_launch_us": round((time.time() - t0) / n * 1e6, 1), "launches": n}
+        try:
+            rec["amd_smi"] = json.loads(proc.communicate(timeout=60)[0]) if proc else None
+        except (ValueError, subprocess.TimeoutExpired, OSError) as err:
+            rec["amd_smi"] = f"unavailable: {err}"
+        out[tag] = rec
+    print(json.dumps(out), flush=True)
 
 
 def make_weights(L, moe, torch):
@@ -185,8 +242,27 @@ def dense_gemm(moe, torch, launches: int = 20) -> dict:
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / launches
     flops = 2.0 * G.M * G.N * G.K
+    del A, W, D, args, ws
+    torch.cuda.empty_cache()
+    # reference: the library fp16 GEMM (torch.matmul on fp16 operands) at the same shape, the
+    # f16 MFMA rate a tuned dense kernel reaches on this machine
+    a = torch.randn(G.M, G.K, dtype=torch.float16, device=dev)
+    b = torch.randn(G.K, G.N, dtype=torch.float16, device=dev)
+    for _ in range(3):
+        c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(launches):
+        c = torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ref_us = e0.elapsed_time(e1) * 1e3 / launches
+    del a, b, c
+    torch.cuda.empty_cache()
     return {"workload": G.name, "avg_launch_us": round(us, 1), "tflops": round(flops / us / 1e6, 1),
-            "frac_of_f16_dense_peak": round(flops / us / 1e6 / F16_PEAK_TFLOPS, 4)}
+            "frac_of_f16_dense_peak": round(flops / us / 1e6 / F16_PEAK_TFLOPS, 4),
+            "torch_f16_matmul_tflops": round(flops / ref_us / 1e6, 1),
+            "frac_of_torch_f16_matmul": round(ref_us / us, 4)}
 
 
 def cpu_baseline(L, offsets, row_src, seconds):
@@ -217,10 +293,44 @@ def cpu_baseline(L, offsets, row_src, seconds):
         rows_done += hi - lo
         if spent >= seconds:
             break
-    return {"value": flops / spent / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"oracle grouped GEMMs (gate/up {2 * L.I}x{L.H} then down {L.H}x{L.I}) over the "
-                      f"{rows_done} routed rows of the first {experts} experts of the same workload, "
-                      f"{spent:.1f} s of CPU time"}
+    rec = {"value": flops / spent / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"oracle grouped GEMMs (gate/up {2 * L.I}x{L.H} then down {L.H}x{L.I}) over the "
+                     f"{rows_done} routed rows of the first {experts} experts of the same workload, "
+                     f"{spent:.1f} s of CPU time"}
+    # the same GEMMs on one thread, over the first few experts (about a quarter of the time)
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        f1, s1, n1, e = 0.0, 0.0, 0, 0
+        while s1 < seconds / 4 and e < L.E:
+            lo, hi = int(offsets[e]), int(offsets[e + 1])
+            e += 1
+            if hi == lo:
+                continue
+            w1 = oracle.quantize(synth.layer_w1(L, e - 1))
+            t0 = time.perf_counter()
+            oracle.grouped_gemm(xq, w1.q[None], w1.sf[None], np.array([w1.g], np.float32),
+                                np.array([0, hi - lo], np.int32), A_rows=row_src[lo:hi])
+            s1 += time.perf_counter() - t0
+            f1 += 2.0 * (hi - lo) * 2 * L.I * L.H
+            n1 += hi - lo
+    finally:
+        oracle.set_num_threads(threads)
+    rec["single_thread"] = {"value": f1 / s1 / 1e12, "unit": "TFLOPS",
+                            "sample": f"oracle gate/up GEMMs over {n1} routed rows, {s1:.1f} s on one thread"}
+    rec["host"] = {"cpu": host_cpu_model(), "nproc": os.cpu_count()}
+    return rec
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def run_layer(L, moe, torch, steps: int, warmup: int, weights=None, fused: bool = False) -> dict:
@@ -308,6 +418,13 @@ def main():
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
         return
+    if args.power_sample:
+        import torch
+
+        import block_scaled_fp4_02_amd as moe
+        torch.cuda.set_device(0)
+        power_sample(moe, torch)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
@@ -359,6 +476,9 @@ def main():
         del f
     del r
     torch.cuda.empty_cache()
+    copy_gbps = copy_bandwidth(torch)
+    rec["roofline"]["measured_copy_GBps"] = round(copy_gbps, 1)
+    rec["roofline"]["frac_of_measured_copy"] = round(rec["roofline"]["achieved"] / copy_gbps, 4)
     if L is synth.LAYER_DECODE:
         rec["grouped_gemm_decode_8x32"] = grouped_gemm_decode(moe, torch, args.steps)
         rec["dense_gemm_8192"] = dense_gemm(moe, torch)

@@ -51,6 +51,7 @@ def lib():
             "orc_swiglu": (None, [P, i64, i32, P]),
             "orc_finalize": (None, [P, P, P, i32, i32, i32, P, P]),
             "orc_num_threads": (i32, []),
+            "orc_set_num_threads": (None, [i32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -199,6 +200,11 @@ def finalize(y2: np.ndarray, w: np.ndarray, token_slot_row: np.ndarray):
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for the following oracle calls."""
+    lib().orc_set_num_threads(int(n))
 
 
 # ---- the whole layer ---------------------------------------------------------

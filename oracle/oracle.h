@@ -114,6 +114,7 @@ void orc_finalize(const double *y2, const double *topk_w,
 
 /* Number of OpenMP threads the oracle runs on. */
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
