@@ -401,13 +401,16 @@ def run_layer(L, moe, torch, steps: int, warmup: int, weights=None, fused: bool 
             "weight_gbps": weight_gbps, "g1_alg_bytes": g1_alg_bytes, "g1_s": g1_s}
 
 
-def shard_record(L, moe, torch, steps: int) -> dict:
-    """One GPU's share of the decode layer under expert or tensor parallelism, full path."""
-    r = run_layer(L, moe, torch, steps, 2)
+def shard_record(L, moe, torch, steps: int, weights=None) -> dict:
+    """A further layer configuration on the full path (one GPU's share of the decode layer
+    under expert or tensor parallelism, or the skewed decode layer); `weights` reuses packed
+    weights of the same shape."""
+    r = run_layer(L, moe, torch, steps, 2, weights=weights)
     out = {"workload": L.name, "ms_per_step": round(r["ms_per_step"], 4), "tflops": round(r["value"], 2),
            "gemm_tflops": round(r["gemm_tflops"], 2), "weight_hbm_GBps": round(r["weight_gbps"], 1),
            "weight_hbm_frac": round(r["weight_gbps"] / HBM_PEAK_GBPS, 4),
-           "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()}}
+           "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
+           "offsets": [int(v) for v in r["off"]]}
     del r
     torch.cuda.empty_cache()
     return out
@@ -474,6 +477,13 @@ def main():
             "note": "SwiGLU output requantised in the gate/up GEMM epilogue (MOE_EPI_SWIGLU_NVFP4) with a "
                     "static global scale calibrated from one dynamic pass; requantize stage is empty"}
         del f
+        # skewed decode (512 tokens, Zipf-biased router: 0-200+ rows per expert, some empty), the
+        # same expert weights; its weight rate counts active experts only
+        sk = shard_record(synth.LAYER_SKEWED, moe, torch, args.steps, weights=r["weights"])
+        sizes_sk = np.diff(np.asarray(sk.pop("offsets")))
+        sk["rows_per_expert_min_median_max"] = [int(sizes_sk.min()), int(np.median(sizes_sk)), int(sizes_sk.max())]
+        sk["active_experts"] = int((sizes_sk > 0).sum())
+        rec["layer_skewed"] = sk
     del r
     torch.cuda.empty_cache()
     copy_gbps = copy_bandwidth(torch)
@@ -482,8 +492,9 @@ def main():
     if L is synth.LAYER_DECODE:
         rec["grouped_gemm_decode_8x32"] = grouped_gemm_decode(moe, torch, args.steps)
         rec["dense_gemm_8192"] = dense_gemm(moe, torch)
-        rec["shard_ep8"] = shard_record(synth.LAYER_EP8, moe, torch, args.steps)
-        rec["shard_tp8"] = shard_record(synth.LAYER_TP8, moe, torch, args.steps)
+        for key, Ls in (("shard_ep8", synth.LAYER_EP8), ("shard_tp8", synth.LAYER_TP8)):
+            rec[key] = shard_record(Ls, moe, torch, args.steps)
+            del rec[key]["offsets"]
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(L, off, row_src, args.cpu_baseline_seconds)
     print(json.dumps(rec), flush=True)
