@@ -163,7 +163,10 @@ moe_status moe_quantize_nvfp4(const void *x, int x_dtype, int64_t rows, int64_t 
  * packed weights), MOE_ERR_UNSUPPORTED otherwise.
  * moe_grouped_gemm_nvfp4_can_implement() returns MOE_OK exactly when the
  * launch is supported; a supported launch then cannot fail on its
- * configuration.  ws: moe_grouped_gemm_nvfp4_workspace(args) bytes.
+ * configuration.  ws: moe_grouped_gemm_nvfp4_workspace(args) bytes.  The
+ * workspace and amax-slot queries read the shapes, layout and epilogue only (the
+ * pointers may still be NULL, so they can size buffers before allocation): they
+ * return 0 exactly when can_implement fails for a reason other than a NULL pointer.
  * ------------------------------------------------------------------------- */
 typedef enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_SWIGLU_NVFP4 = 2 } moe_epilogue;
 typedef enum moe_layout { MOE_LAYOUT_ROWMAJOR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout;

@@ -175,3 +175,52 @@ def test_header_is_c11_and_matches_the_binding(tmp_path):
         assert got[f"off {f}"] == getattr(m.moe_gemm_args, f).offset, f
     for c in consts:
         assert got[f"const {c}"] == getattr(m, c), c
+
+
+def test_host_queries_survive_random_and_hostile_arguments():
+    """Seeded fuzz of the host-only entry points (no launch is ever attempted): for random,
+    often invalid shapes, layouts, epilogues and NULL pointers, can_implement returns a
+    documented status, and the workspace and amax-slot queries (shapes only) are non-zero
+    exactly when can_implement fails for no reason but a NULL pointer; the quantiser and
+    routing workspace queries never fail."""
+    import numpy as np
+    L = moe.lib()
+    rng = np.random.default_rng(1234)
+    ptrs = ("A", "A_sf", "A_gs", "A_rows", "B", "B_sf", "B_gs", "expert_offsets", "D", "amax_out", "D_sf", "D_gs")
+
+    def dim(mults=(16, 256, 512)):
+        kind = rng.integers(0, 5)
+        if kind == 0:
+            return int(rng.integers(-300, 300))
+        if kind == 1:
+            return int(rng.choice(mults)) * int(rng.integers(0, 40))
+        if kind == 2:
+            return int(rng.integers(0, 1 << 31))
+        return int(rng.choice(mults)) * int(rng.integers(1, 64))
+
+    seen = set()
+    for _ in range(4000):
+        a = moe.moe_gemm_args()
+        for f in ptrs:
+            setattr(a, f, None if rng.random() < 0.08 else FAKE)
+        a.E = int(rng.choice([-1, 0, 1, 8, 256, 65536, 65537, int(rng.integers(1, 5000))]))
+        a.N, a.K = dim(), dim()
+        a.R = int(rng.choice([-1, 0, 1, 256, 8192, 1 << 31, 1 << 40, int(rng.integers(0, 1 << 20))]))
+        a.rows_A = int(rng.choice([-1, 0, a.R if a.R >= 0 else 0, 1 << 33, int(rng.integers(0, 1 << 20))]))
+        a.epilogue = int(rng.integers(-1, 4))
+        a.B_layout = int(rng.integers(-1, 3))
+        st = L.moe_grouped_gemm_nvfp4_can_implement(C.byref(a))
+        assert st in (moe.MOE_OK, moe.MOE_ERR_NULL, moe.MOE_ERR_SHAPE, moe.MOE_ERR_UNSUPPORTED), st
+        ws = L.moe_grouped_gemm_nvfp4_workspace(C.byref(a))
+        slots = L.moe_grouped_gemm_nvfp4_amax_slots(C.byref(a))
+        if st in (moe.MOE_OK, moe.MOE_ERR_NULL):
+            assert ws > 0 and slots > 0, st
+        else:
+            assert ws == 0 and slots == 0, st
+        seen.add(st)
+    assert seen == {moe.MOE_OK, moe.MOE_ERR_NULL, moe.MOE_ERR_SHAPE, moe.MOE_ERR_UNSUPPORTED}
+    for _ in range(2000):
+        rows, cols = int(rng.integers(-5, 1 << 24)), int(rng.integers(-5, 1 << 16))
+        L.moe_quantize_nvfp4_workspace(rows, cols)
+        T, E, k = int(rng.integers(-5, 1 << 20)), int(rng.integers(-5, 2000)), int(rng.integers(-5, 40))
+        L.moe_route_permute_workspace(T, E, k)
