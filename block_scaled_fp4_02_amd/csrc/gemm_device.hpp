@@ -43,8 +43,8 @@ struct Params {
 };
 
 // Largest expert count for which waves derive their work item from the offsets themselves
-// (one wave-wide pass each for the count and the item); above it, repeating the passes in
-// thousands of workgroups costs more than one schedule kernel that writes the item list.
+// (one wave-wide pass, an expert per lane); above it, repeating the pass in thousands of
+// workgroups costs more than one schedule kernel that writes the item list.
 constexpr int kMaxInlineScheduleExperts = 64;
 
 // Rows of expert e (offsets clamped to [0, R] and made monotone) and its first row.
@@ -54,12 +54,6 @@ __device__ __forceinline__ int expert_rows(const Params &P, int e, int64_t &lo) 
   int64_t hi = P.offsets[e + 1];
   hi = hi < lo ? lo : (hi > P.R ? P.R : hi);
   return static_cast<int>(hi - lo);
-}
-
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
@@ -74,63 +68,48 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 
 // Work item of workgroup b, or false if it has none.  Workgroup b runs on XCD b % 8, so
 // the items are dealt to XCDs in contiguous ranges: neighbouring items (the n tiles and row
-// chunks of one expert) share that XCD's L2.  The result is wave-uniform.
+// chunks of one expert) share that XCD's L2.  The result is wave-uniform.  Without an item
+// list (at most kMaxInlineScheduleExperts = 64 experts) lane e reads the offsets of expert e
+// once and the wave derives the count and the item from them in one pass.
+static_assert(kMaxInlineScheduleExperts <= kWave, "inline scheduling keeps one expert per lane");
 __device__ __forceinline__ bool item_for_block(const Params &P, int b, int4 &item) {
-  const int lane = threadIdx.x & 63;
-  const int cr = P.chunk_rows;
-  int count;
-  if (P.items) {
-    count = *P.count;
-  } else {
-    count = 0;
-    for (int base = 0; base < P.E; base += kWave) {
-      const int e = base + lane;
-      int mine = 0;
-      if (e < P.E) {
-        int64_t lo;
-        mine = (expert_rows(P, e, lo) + cr - 1) / cr * P.n_tiles;
-      }
-      count += wave_sum(mine);
-    }
-    count = __builtin_amdgcn_readfirstlane(count);   // uniform: keep it (and w) in SGPRs
-  }
-  const int per_xcd = (count + kXcds - 1) / kXcds;
   const int jx = b / kXcds;
-  const int w = (b % kXcds) * per_xcd + jx;
-  if (jx >= per_xcd || w >= count) return false;
   if (P.items) {
+    const int count = *P.count;
+    const int per_xcd = (count + kXcds - 1) / kXcds;
+    const int w = (b % kXcds) * per_xcd + jx;
+    if (jx >= per_xcd || w >= count) return false;
     item = P.items[w];
     return true;
   }
-  int carry = 0;   // items of the experts before this group of 64
-  for (int base = 0; base < P.E; base += kWave) {
-    const int e = base + lane;
-    int64_t lo = 0;
-    int rows = 0, chunks = 0;
-    if (e < P.E) {
-      rows = expert_rows(P, e, lo);
-      chunks = (rows + cr - 1) / cr;
-    }
-    const int mine = chunks * P.n_tiles;
-    const int incl = wave_inclusive_scan(mine);
-    const int local = w - carry - (incl - mine);   // index of w among expert e's items
-    const uint64_t owner = __ballot(mine > 0 && local >= 0 && local < mine);
-    if (owner) {
-      // the owner lane's values, read as scalars so that everything the kernel derives
-      // from the item stays in SGPRs
-      const int src = __builtin_ctzll(owner);
-      const int c_src = __builtin_amdgcn_readlane(chunks, src);
-      const int l_src = __builtin_amdgcn_readlane(local, src);
-      const int rows_src = __builtin_amdgcn_readlane(rows, src);
-      const int lo_src = __builtin_amdgcn_readlane(static_cast<int>(lo), src);
-      const int nt = l_src / c_src, c = l_src % c_src;
-      const int nr = rows_src - c * cr;
-      item = make_int4(base + src, lo_src + c * cr, nr < cr ? nr : cr, nt);
-      return true;
-    }
-    carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+  const int lane = threadIdx.x & 63;
+  const int cr = P.chunk_rows;
+  int64_t lo = 0;
+  int rows = 0, chunks = 0;
+  if (lane < P.E) {
+    rows = expert_rows(P, lane, lo);
+    chunks = (rows + cr - 1) / cr;
   }
-  return false;   // not reached: w < count
+  const int mine = chunks * P.n_tiles;
+  const int incl = wave_inclusive_scan(mine);
+  // uniform: keep the count, and everything derived from it, in SGPRs
+  const int count = __builtin_amdgcn_readlane(incl, kWave - 1);
+  const int per_xcd = (count + kXcds - 1) / kXcds;
+  const int w = (b % kXcds) * per_xcd + jx;
+  if (jx >= per_xcd || w >= count) return false;
+  const int local = w - (incl - mine);   // index of w among expert `lane`'s items
+  const uint64_t owner = __ballot(mine > 0 && local >= 0 && local < mine);
+  // the owner lane's values, read as scalars so that everything the kernel derives from the
+  // item stays in SGPRs (w < count, so exactly one lane owns it)
+  const int src = __builtin_ctzll(owner);
+  const int c_src = __builtin_amdgcn_readlane(chunks, src);
+  const int l_src = __builtin_amdgcn_readlane(local, src);
+  const int rows_src = __builtin_amdgcn_readlane(rows, src);
+  const int lo_src = __builtin_amdgcn_readlane(static_cast<int>(lo), src);
+  const int nt = l_src / c_src, c = l_src % c_src;
+  const int nr = rows_src - c * cr;
+  item = make_int4(src, lo_src + c * cr, nr < cr ? nr : cr, nt);
+  return true;
 }
 
 // ---- dequantisation ------------------------------------------------------------------

@@ -185,6 +185,13 @@ GemmPlan plan_gemm(const moe_gemm_args &a) {
   const int64_t chunk_bound = (a.R + p.chunk_rows - 1) / p.chunk_rows + a.E;
   p.max_items = static_cast<int64_t>(p.n_tiles) * chunk_bound;
   p.grid = (p.max_items + kXcds - 1) / kXcds * kXcds;
+  if (p.kernel == kKSplit) {
+    // the K-split kernel loops over its items: launch no more workgroups than fit on the
+    // chip at once (256 CUs; one 8-wave or two 4-wave workgroups per CU), so that no empty
+    // workgroup waits for a CU at the end (a multiple of the 8 XCDs)
+    const int64_t resident = static_cast<int64_t>(256) * (8 / ksplit_waves(p.ks));
+    p.grid = std::min<int64_t>(p.grid, resident);
+  }
   p.inline_schedule = a.E <= kMaxInlineScheduleExperts;
   p.ws_bytes = p.inline_schedule ? 16 : 16 + static_cast<size_t>(p.max_items) * sizeof(int4);
   return p;
