@@ -113,6 +113,24 @@ def test_gemm_can_implement_is_truthful_on_shapes():
     assert L.moe_grouped_gemm_nvfp4(C.byref(ok), None, ws, None) == moe.MOE_ERR_WORKSPACE
 
 
+def test_ksplit_grid_is_capped_at_resident_workgroups():
+    """The K-split kernel loops over its work items, so its grid (= the partial-maxima slot
+    count) stops at the workgroups that fit on the chip at once -- 256 CUs x one 8-wave or two
+    4-wave workgroups -- while the item count can exceed it; the other kernels keep the host's
+    upper bound on the items."""
+    L = moe.lib()
+    slots = lambda **kw: L.moe_grouped_gemm_nvfp4_amax_slots(C.byref(gemm_args(layout=1, **kw)))
+    # 8 groups x 32 rows, K 6144: split 8 ways, 256 items (one per workgroup)
+    assert slots(E=8, N=2048, K=6144, R=256) == 256
+    # 14 groups x 33 rows, K 2048: split 8 ways; 14 x 2 chunks x 32 n tiles = 896 items
+    assert slots(E=14, N=2048, K=2048, R=462) == 256
+    # 32 groups x 33 rows, K 512: split 2 ways (4-wave workgroups, 128-row n tiles);
+    # 32 x 2 x 16 = 1024 items
+    assert slots(E=32, N=2048, K=512, R=1056) == 512
+    # the decode layer's 256 experts use the LDS kernel: (ceil(8192 / 48) + 256) x 16 items
+    assert slots(E=256, N=4096, K=6144, R=8192) == (8192 // 48 + 1 + 256) * 16
+
+
 def test_gemm_workspace_grows_with_rows_and_experts():
     L = moe.lib()
     small = L.moe_grouped_gemm_nvfp4_workspace(C.byref(gemm_args(E=8, R=256)))

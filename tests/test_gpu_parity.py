@@ -211,6 +211,8 @@ def _run_gemm_none(A, Bs, off, A_rows, R, label, packed=False):
     ([40, 0, 3], 1536, 256, False),                       # K split 2 ways inside a workgroup
     ([7, 25], 1024, 512, False),                          # K split 4 ways
     ([45, 3], 2048, 256, True),                           # K split 8 ways, 32 + 13 row chunks
+    ([33] * 14, 2048, 2048, True),                        # K split 8 ways: 896 items looped over 256 workgroups
+    ([33] * 32, 512, 2048, False),                        # K split 2 ways: 1024 items looped over 512 workgroups
     ([0, 1, 2, 3, 5, 8, 13] * 150 + [40, 0], 256, 256, True),  # 1052 experts: two scan blocks in the schedule
     ([0, 0, 0], 256, 256, False),                         # no rows at all
     ([300], 256, 768, True),                              # one big group: several row chunks
@@ -320,7 +322,8 @@ def _run_gemm_swiglu(A, Bs, off, A_rows, R, label, rows=None, packed=False):
 @pytest.mark.parametrize("sizes,K,I", [([8, 6, 9, 9], 256, 256), ([0, 17, 33, 64, 65, 1], 512, 384),
                                        ([40] * 256 + [3, 0, 64], 256, 512),
                                        ([0, 130, 255, 97], 768, 256),    # several chunks, odd K steps
-                                       ([20, 32], 2048, 256)])           # K split 8 ways
+                                       ([20, 32], 2048, 256),            # K split 8 ways
+                                       ([33] * 14, 2048, 1024)])         # K split 8 ways, items looped
 def test_gemm_swiglu_shapes(sizes, K, I, packed):
     A, Bs, off, A_rows, R = _gemm_case(sizes, K, 2 * I, True, seed=7 + K + I)
     _run_gemm_swiglu(A, Bs, off, A_rows, R, f"sizes={sizes}", packed=packed)
@@ -329,6 +332,7 @@ def test_gemm_swiglu_shapes(sizes, K, I, packed):
 @pytest.mark.parametrize("sizes,K,I,g_div", [([8, 6, 9, 9], 256, 256, 1.0), ([0, 17, 33, 64, 65, 1], 512, 384, 4.0),
                                              ([40] * 256 + [3, 0, 64], 256, 512, 1.0),   # LDS kernel
                                              ([20, 32], 2048, 256, 1.0),                 # K split 8 ways
+                                             ([33] * 14, 2048, 1024, 1.0),               # K split, items looped
                                              ([0, 130, 255, 97], 768, 256, 2.0)])        # 8-wave kernel
 def test_gemm_swiglu_nvfp4_fused(sizes, K, I, g_div):
     """SwiGLU + NVFP4 epilogue with a static global scale g2: codes and scales equal the
