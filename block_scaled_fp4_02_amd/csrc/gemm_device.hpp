@@ -66,13 +66,20 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
-// Work item of workgroup b, or false if it has none.  Workgroup b runs on XCD b % 8, so
+// The schedule kernel stores an item's n tile with this bit set when the item is the last
+// row chunk of its expert: the launch's final read of that n tile's weights, which the
+// packed-weight kernels then load with the non-temporal hint (earlier chunks re-read the
+// same weights from L2, so they keep the default policy).
+constexpr int kLastChunkFlag = 1 << 30;
+
+// Work item of workgroup b, or false if it has none; `last` is true for the last row chunk
+// of the item's expert.  Workgroup b runs on XCD b % 8, so
 // the items are dealt to XCDs in contiguous ranges: neighbouring items (the n tiles and row
 // chunks of one expert) share that XCD's L2.  The result is wave-uniform.  Without an item
 // list (at most kMaxInlineScheduleExperts = 64 experts) lane e reads the offsets of expert e
 // once and the wave derives the count and the item from them in one pass.
 static_assert(kMaxInlineScheduleExperts <= kWave, "inline scheduling keeps one expert per lane");
-__device__ __forceinline__ bool item_for_block(const Params &P, int b, int4 &item) {
+__device__ __forceinline__ bool item_for_block(const Params &P, int b, int4 &item, bool &last) {
   const int jx = b / kXcds;
   if (P.items) {
     const int count = *P.count;
@@ -80,6 +87,8 @@ __device__ __forceinline__ bool item_for_block(const Params &P, int b, int4 &ite
     const int w = (b % kXcds) * per_xcd + jx;
     if (jx >= per_xcd || w >= count) return false;
     item = P.items[w];
+    last = (item.w & kLastChunkFlag) != 0;
+    item.w &= ~kLastChunkFlag;
     return true;
   }
   const int lane = threadIdx.x & 63;
@@ -109,7 +118,13 @@ __device__ __forceinline__ bool item_for_block(const Params &P, int b, int4 &ite
   const int nt = l_src / c_src, c = l_src % c_src;
   const int nr = rows_src - c * cr;
   item = make_int4(src, lo_src + c * cr, nr < cr ? nr : cr, nt);
+  last = c == c_src - 1;
   return true;
+}
+
+__device__ __forceinline__ bool item_for_block(const Params &P, int b, int4 &item) {
+  bool last;
+  return item_for_block(P, b, item, last);
 }
 
 // ---- dequantisation ------------------------------------------------------------------
@@ -189,13 +204,18 @@ __device__ __forceinline__ BufRsrc make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
 
+// Cache-policy operand of a buffer load: 0 (default) or kNonTemporal (the gfx950 "nt" bit:
+// the lines are streamed, not kept for reuse).
+constexpr int kNonTemporal = 2;
+
+template <int POLICY = 0>
 __device__ __forceinline__ void load_frag16_buf(Frag16 &f, BufRsrc rc, uint32_t code_off, uint32_t qs, BufRsrc rs,
                                                 uint32_t scale_off) {
-  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rc, code_off, 0, 0);
-  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rc, code_off + qs, 0, 0);
+  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rc, code_off, 0, POLICY);
+  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rc, code_off + qs, 0, POLICY);
   f.q[0] = make_uint4(a.x, a.y, a.z, a.w);
   f.q[1] = make_uint4(b.x, b.y, b.z, b.w);
-  f.s = __builtin_amdgcn_raw_buffer_load_b32(rs, scale_off, 0, 0);
+  f.s = __builtin_amdgcn_raw_buffer_load_b32(rs, scale_off, 0, POLICY);
 }
 
 // ---- epilogue ---------------------------------------------------------------------------

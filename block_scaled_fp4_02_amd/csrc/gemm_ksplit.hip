@@ -15,7 +15,8 @@
 // complete only once nearly all data has arrived, so no wave starts computing until late;
 // with one half step of lead, data arrives roughly in the order it is used.  All loads are
 // unconditional range-checked buffer loads (past the wave's K range they return zeros and
-// read nothing), so the compiler counts the loads in flight exactly.
+// read nothing), so the compiler counts the loads in flight exactly; the weight loads of an
+// expert's last row chunk carry the non-temporal hint.
 //
 // After the K loop every wave parks its partial tile in LDS; then the waves of a row group
 // share the reduction and the epilogue, each summing the KS partials of its own (weight
@@ -42,11 +43,12 @@ struct Half16 {
   uint32_t s;
 };
 
+template <int POLICY = 0>
 __device__ __forceinline__ void load_half16_buf(Half16 &f, BufRsrc rc, uint32_t code_off, BufRsrc rs,
                                                 uint32_t scale_off) {
-  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rc, code_off, 0, 0);
+  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rc, code_off, 0, POLICY);
   f.q = make_uint4(a.x, a.y, a.z, a.w);
-  f.s = __builtin_amdgcn_raw_buffer_load_b16(rs, scale_off, 0, 0);
+  f.s = __builtin_amdgcn_raw_buffer_load_b16(rs, scale_off, 0, POLICY);
 }
 
 // First weight row of 16-row tile j (0..3) of row group ng in n tile nt.  SwiGLU tiles are
@@ -78,8 +80,9 @@ __device__ __forceinline__ float4v sum_partials(const float *red, int ng, int j,
 }
 
 // One work item (expert e, rows [row0, row0 + nrows), n tile nt); returns the wave's
-// max |act| for the SWIGLU epilogue (0 otherwise).
-template <int NM, int KS, int EPI>
+// max |act| for the SWIGLU epilogue (0 otherwise).  NT: the expert's last row chunk, whose
+// weight loads carry the non-temporal hint.
+template <int NM, int KS, int EPI, bool NT>
 __device__ __forceinline__ float ks_body(const Params &P, float *red, int e, int row0, int nrows, int nt) {
   constexpr int WAVES = split_waves<KS>();
   constexpr int NG = WAVES / KS;
@@ -122,7 +125,8 @@ __device__ __forceinline__ float ks_body(const Params &P, float *red, int e, int
     const uint32_t so = h < halves ? static_cast<uint32_t>(s_begin + (h >> 1)) * kPackBlock : kOob;
     const uint32_t q = static_cast<uint32_t>(h & 1);
 #pragma unroll
-    for (int j = 0; j < 4; j++) load_half16_buf(f[j], rb, b_code[j] + so + q * 1024, rb, b_scale[j] + so + 2 * q);
+    for (int j = 0; j < 4; j++)
+      load_half16_buf<NT ? kNonTemporal : 0>(f[j], rb, b_code[j] + so + q * 1024, rb, b_scale[j] + so + 2 * q);
   };
   auto load_a = [&](Half16 (&f)[NM], int h) {
     const bool v = h < halves;
@@ -238,9 +242,13 @@ __global__ __launch_bounds__(64 * split_waves<KS>(), 8 / split_waves<KS>()) void
   float amax = 0.f;
   for (int vb = blockIdx.x;; vb += gridDim.x) {   // a multiple of 8 apart: the same XCD
     int4 item;
-    if (!item_for_block(P, vb, item)) break;
-    const float m = item.z <= 16 ? ks_body<1, KS, EPI>(P, red, item.x, item.y, item.z, item.w)
-                                 : ks_body<2, KS, EPI>(P, red, item.x, item.y, item.z, item.w);
+    bool last;
+    if (!item_for_block(P, vb, item, last)) break;
+    float m;
+    if (last) m = item.z <= 16 ? ks_body<1, KS, EPI, true>(P, red, item.x, item.y, item.z, item.w)
+                               : ks_body<2, KS, EPI, true>(P, red, item.x, item.y, item.z, item.w);
+    else m = item.z <= 16 ? ks_body<1, KS, EPI, false>(P, red, item.x, item.y, item.z, item.w)
+                          : ks_body<2, KS, EPI, false>(P, red, item.x, item.y, item.z, item.w);
     amax = fmaxf(amax, m);
     __syncthreads();   // the next item rewrites the partial tiles
   }

@@ -19,6 +19,8 @@
 //    behind a branch makes it wait for all of them).
 //  * NM (token tiles of the item) is a template parameter, so the K loop is straight-line
 //    code.
+//  * The expert's last row chunk loads its weights with the non-temporal hint (no later item
+//    of the launch reads them again); earlier chunks keep them in L2 for the next chunk.
 // Chunks of up to 48 rows (three token tiles), 48 KB of LDS and at most 168 VGPRs, so three
 // workgroups share a CU and overlap one another's loads, dequantisation and MFMAs.  Per step
 // and wave: 264 VALU (weight dequantisation) for 32*NM MFMAs.  At decode sizes the kernel
@@ -38,7 +40,7 @@ struct LdsShared {
   float wmax[WAVES];
 };
 
-template <int NM, int EPI, int MAXT, int WAVES>
+template <int NM, int EPI, bool NT, int MAXT, int WAVES>
 __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES> &sh, int b, int e, int row0, int nrows,
                                          int nt) {
   constexpr int SPAN = 64 * WAVES;                  // weight rows per workgroup
@@ -116,7 +118,8 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
   auto load_b = [&](Frag16 (&f)[4], int s) {
     const uint32_t so = s < steps ? static_cast<uint32_t>(s) * kPackBlock : kOob;
 #pragma unroll
-    for (int j = 0; j < 4; j++) load_frag16_buf(f[j], rb, b_code[j] + so, 1024, rb, b_scale[j] + so);
+    for (int j = 0; j < 4; j++)
+      load_frag16_buf<NT ? kNonTemporal : 0>(f[j], rb, b_code[j] + so, 1024, rb, b_scale[j] + so);
   };
 
   float4v acc[4][NM];
@@ -236,14 +239,21 @@ __global__ __launch_bounds__(256, 3) void gemm_lds_kernel(Params P) {
   __shared__ LdsShared<kChunkTiles, 4> sh;
   const int b = blockIdx.x;
   int4 item;
-  if (!item_for_block(P, b, item)) {
+  bool last;
+  if (!item_for_block(P, b, item, last)) {
     if (EPI == MOE_EPI_SWIGLU && threadIdx.x == 0) P.amax_out[b] = 0.f;
     return;
   }
   const int nm = (item.z + 15) / 16;   // workgroup-uniform
-  if (nm <= 1) lds_body<1, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
-  else if (nm == 2) lds_body<2, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
-  else lds_body<3, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
+  if (last) {   // the expert's last chunk: no later item re-reads these weights
+    if (nm <= 1) lds_body<1, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
+    else if (nm == 2) lds_body<2, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
+    else lds_body<3, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
+  } else {
+    if (nm <= 1) lds_body<1, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
+    else if (nm == 2) lds_body<2, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
+    else lds_body<3, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
+  }
 }
 
 // Hundreds of rows per expert: eight waves share one activation tile of up to six token
@@ -255,14 +265,21 @@ __global__ __launch_bounds__(512, 1) void gemm_lds_wide_kernel(Params P) {
   __shared__ LdsShared<kWideChunkTiles, 8> sh;
   const int b = blockIdx.x;
   int4 item;
-  if (!item_for_block(P, b, item)) {
+  bool last;
+  if (!item_for_block(P, b, item, last)) {
     if (EPI == MOE_EPI_SWIGLU && threadIdx.x == 0) P.amax_out[b] = 0.f;
     return;
   }
   const int nm = (item.z + 15) / 16;   // workgroup-uniform
-  if (nm <= 2) lds_body<2, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
-  else if (nm <= 4) lds_body<4, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
-  else lds_body<6, EPI>(P, sh, b, item.x, item.y, item.z, item.w);
+  if (last) {
+    if (nm <= 2) lds_body<2, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
+    else if (nm <= 4) lds_body<4, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
+    else lds_body<6, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
+  } else {
+    if (nm <= 2) lds_body<2, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
+    else if (nm <= 4) lds_body<4, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
+    else lds_body<6, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
+  }
 }
 
 }  // namespace

@@ -11,7 +11,7 @@
 //
 // Design (not the pages' SM120 tiles; this is for gfx950):
 //  * Work list: items (expert, row chunk, n tile), ordered expert-major, then n tile, then
-//    chunk.  Up to 64 experts every wave derives its own item from expert_offsets (a
+//    chunk; the last chunk of an expert is flagged (its weight loads are non-temporal).  Up to 64 experts every wave derives its own item from expert_offsets (a
 //    wave-wide sum and scan, no extra launch); above that a schedule kernel writes the list
 //    first (each of its workgroups scans the offsets and writes a slice of the items).  The grid is the host-side upper bound on the
 //    item count; items past the device-side count exit.
@@ -90,7 +90,8 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
       const int local = w - (incl[a] - ch * n_tiles);
       const int nt = local / ch, c = local - nt * ch;
       const int nr = n_rows[a] - c * chunk_rows;
-      items[carry + w] = make_int4(base + a, first_row[a] + c * chunk_rows, nr < chunk_rows ? nr : chunk_rows, nt);
+      items[carry + w] = make_int4(base + a, first_row[a] + c * chunk_rows, nr < chunk_rows ? nr : chunk_rows,
+                                   nt | (c == ch - 1 ? kLastChunkFlag : 0));
     }
     carry += block_items;
     __syncthreads();
