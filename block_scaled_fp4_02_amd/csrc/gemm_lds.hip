@@ -19,8 +19,9 @@
 //    behind a branch makes it wait for all of them).
 //  * NM (token tiles of the item) is a template parameter, so the K loop is straight-line
 //    code.
-//  * The expert's last row chunk loads its weights with the non-temporal hint (no later item
-//    of the launch reads them again); earlier chunks keep them in L2 for the next chunk.
+//  * In the four-wave kernel the expert's last row chunk loads its weights with the
+//    non-temporal hint (no later item of the launch reads them again); earlier chunks keep
+//    them in L2 for the next chunk.
 // Chunks of up to 48 rows (three token tiles), 48 KB of LDS and at most 168 VGPRs, so three
 // workgroups share a CU and overlap one another's loads, dequantisation and MFMAs.  Per step
 // and wave: 264 VALU (weight dequantisation) for 32*NM MFMAs.  At decode sizes the kernel
@@ -265,21 +266,17 @@ __global__ __launch_bounds__(512, 1) void gemm_lds_wide_kernel(Params P) {
   __shared__ LdsShared<kWideChunkTiles, 8> sh;
   const int b = blockIdx.x;
   int4 item;
-  bool last;
-  if (!item_for_block(P, b, item, last)) {
+  if (!item_for_block(P, b, item)) {
     if (EPI == MOE_EPI_SWIGLU && threadIdx.x == 0) P.amax_out[b] = 0.f;
     return;
   }
+  // default cache policy throughout: an expert's ~6 chunks run side by side on one XCD, and
+  // non-temporal loads in its last chunk evicted lines its siblings were still reading
+  // (prefill GEMMs +3 %)
   const int nm = (item.z + 15) / 16;   // workgroup-uniform
-  if (last) {
-    if (nm <= 2) lds_body<2, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
-    else if (nm <= 4) lds_body<4, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
-    else lds_body<6, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
-  } else {
-    if (nm <= 2) lds_body<2, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
-    else if (nm <= 4) lds_body<4, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
-    else lds_body<6, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
-  }
+  if (nm <= 2) lds_body<2, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
+  else if (nm <= 4) lds_body<4, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
+  else lds_body<6, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
 }
 
 }  // namespace
