@@ -96,6 +96,9 @@ __device__ __forceinline__ float ks_body(const Params &P, float *red, int e, int
   const int steps = P.K / kKStep;
   const int iters = steps / KS;
   const int s_begin = kq * iters;
+  // global scales, loaded at the start: left in the epilogue the compiler issues these
+  // loads after the last MFMA and waits a full memory round trip for them
+  const float gscale = (*P.A_gs) * P.B_gs[e];
 
   const uint32_t expert_bytes = static_cast<uint32_t>(P.N / 16) * steps * kPackBlock;
   const BufRsrc rb = make_rsrc(P.B + static_cast<int64_t>(e) * expert_bytes, expert_bytes);
@@ -190,7 +193,6 @@ __device__ __forceinline__ float ks_body(const Params &P, float *red, int e, int
   __syncthreads();
 
   // epilogue: 16x16 D lane layout -- weight row 4g + i of the tile, token row r
-  const float gscale = (*P.A_gs) * P.B_gs[e];
   float amax = 0.f;
   if constexpr (EPI == MOE_EPI_NONE) {
     for (int u = kq; u < 4 * NM; u += KS) {   // unit u = (weight tile u / NM, token tile u % NM)

@@ -53,6 +53,9 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
   const int g = lane >> 4;
   const int I = P.N / 2;
   const int steps = P.K / kKStep;
+  // global scales, loaded at the start: left in the epilogue the compiler issues these
+  // loads after the last MFMA and waits a full memory round trip for them
+  const float gscale = (*P.A_gs) * P.B_gs[e];
 
   int nrow[4];   // first weight row of the wave's four tiles (SwiGLU: gate, gate, up, up)
 #pragma unroll
@@ -175,7 +178,6 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
   if (s < steps) step(f0, f1, s);
 
   // epilogue: 16x16 D lane layout -- weight row 4g + i, token row r of the tile
-  const float gscale = (*P.A_gs) * P.B_gs[e];
   if constexpr (EPI == MOE_EPI_SWIGLU_NVFP4) {
     const float g2 = *P.D_gs;
 #pragma unroll
