@@ -127,6 +127,8 @@ def test_ksplit_grid_is_capped_at_resident_workgroups():
     # 32 groups x 33 rows, K 512: split 2 ways (4-wave workgroups, 128-row n tiles);
     # 32 x 2 x 16 = 1024 items
     assert slots(E=32, N=2048, K=512, R=1056) == 512
+    # 100 experts (a schedule kernel writes the item list), K 2048, N 256: split 8 ways
+    assert slots(E=100, N=256, K=2048, R=141) == 256
     # the decode layer's 256 experts use the LDS kernel: (ceil(8192 / 48) + 256) x 16 items
     assert slots(E=256, N=4096, K=6144, R=8192) == (8192 // 48 + 1 + 256) * 16
 

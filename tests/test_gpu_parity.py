@@ -213,6 +213,7 @@ def _run_gemm_none(A, Bs, off, A_rows, R, label, packed=False):
     ([45, 3], 2048, 256, True),                           # K split 8 ways, 32 + 13 row chunks
     ([33] * 14, 2048, 2048, True),                        # K split 8 ways: 896 items looped over 256 workgroups
     ([33] * 32, 512, 2048, False),                        # K split 2 ways: 1024 items looped over 512 workgroups
+    ([1] * 60 + [0, 40, 2] + [1] * 37, 2048, 256, True),  # 100 experts, K split 8 ways: listed items looped
     ([0, 1, 2, 3, 5, 8, 13] * 150 + [40, 0], 256, 256, True),  # 1052 experts: two scan blocks in the schedule
     ([0, 0, 0], 256, 256, False),                         # no rows at all
     ([300], 256, 768, True),                              # one big group: several row chunks
