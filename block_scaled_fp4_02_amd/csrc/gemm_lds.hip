@@ -53,9 +53,6 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
   const int g = lane >> 4;
   const int I = P.N / 2;
   const int steps = P.K / kKStep;
-  // global scales, loaded at the start: left in the epilogue the compiler issues these
-  // loads after the last MFMA and waits a full memory round trip for them
-  const float gscale = (*P.A_gs) * P.B_gs[e];
 
   int nrow[4];   // first weight row of the wave's four tiles (SwiGLU: gate, gate, up, up)
 #pragma unroll
@@ -143,6 +140,10 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
   load_b(f0, 0);
   store_a(ra0, 0);
   __syncthreads();
+  // global scales, loaded during the first step: left in the epilogue the compiler issues
+  // these loads after the last MFMA and waits a full round trip for them; before the first
+  // barrier they delay it
+  const float gscale = (*P.A_gs) * P.B_gs[e];
 
   auto step = [&](const Frag16 (&fb)[4], Frag16 (&fl)[4], int s) {
     const int buf = s & 1;
