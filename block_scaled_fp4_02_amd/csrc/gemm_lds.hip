@@ -45,7 +45,13 @@ template <int NM, int EPI, bool NT, int MAXT, int WAVES>
 __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES> &sh, int b, int e, int row0, int nrows,
                                          int nt) {
   constexpr int SPAN = 64 * WAVES;                  // weight rows per workgroup
-  constexpr int TPW = (MAXT + WAVES - 1) / WAVES;   // token tiles a wave dequantises per step
+  // Activation tiles are dequantised by the first AW waves only.  In the 8-wave kernel the
+  // first wave on each SIMD (the older one, which the SIMD issues from first) otherwise
+  // reaches every step's barrier well ahead of its partner (per-wave timestamps: 26-28 % of
+  // its K loop spent waiting there, against 1-5 % for the second wave), so it takes the
+  // activation work.
+  constexpr int AW = WAVES == 8 ? 4 : WAVES;
+  constexpr int TPW = (MAXT + AW - 1) / AW;   // token tiles a dequantising wave handles per step
   static_assert(NM <= MAXT, "token tiles exceed the LDS buffer");
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -73,7 +79,7 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
     b_scale[j] = static_cast<uint32_t>(nrow[j] / 16) * steps * kPackBlock + 2048 + lane * 4;
   }
 
-  // token tiles wv + WAVES * i this wave dequantises (wave-uniform validity)
+  // token tiles wv + AW * i this wave dequantises (wave-uniform validity)
   const uint32_t half_k = P.K / 2, k16 = P.K / 16;
   const BufRsrc ra_codes = make_rsrc(P.A, static_cast<uint32_t>(P.rows_A * half_k));
   const BufRsrc ra_scales = make_rsrc(P.A_sf, static_cast<uint32_t>(P.rows_A * k16));
@@ -81,8 +87,8 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
   uint32_t a_code[TPW], a_scale[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; i++) {
-    const int t = wv + WAVES * i;
-    a_tile[i] = t < NM;
+    const int t = wv + AW * i;
+    a_tile[i] = wv < AW && t < NM;
     a_code[i] = a_scale[i] = 0;
     if (a_tile[i]) {
       const int m = t * 16 + r;
@@ -111,7 +117,7 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
 #pragma unroll
         for (int d = 0; d < 4; d++) {
           const half8 v = dequant8(word(f[i].q[q], d), sc[d >> 1]);
-          sh.a[buf][wv + WAVES * i][4 * q + d][lane] = __builtin_bit_cast(uint4, v);
+          sh.a[buf][wv + AW * i][4 * q + d][lane] = __builtin_bit_cast(uint4, v);
         }
       }
     }
