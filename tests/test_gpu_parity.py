@@ -231,6 +231,40 @@ def test_gemm_none_shapes(sizes, K, N, gather, packed):
     _run_gemm_none(A, Bs, off, A_rows, R, f"sizes={sizes}", packed)
 
 
+def _random_gemm_shape(seed):
+    """A seeded random grouped-GEMM shape: expert count on both sides of the in-kernel item
+    lookup threshold (64) and of the K-split choice, ragged and empty groups, K and N in the
+    supported multiples; bounded so that the oracle finishes in about a second."""
+    rng = np.random.default_rng(9000 + seed)
+    E = int(rng.choice([1, 3, 8, 24, 64, 65, 100, 257]))
+    K = int(rng.choice([256, 512, 1024, 2048]))
+    N = int(rng.choice([256, 512, 768, 1024]))
+    while E * N * K > 48 * 2 ** 20 and N > 256:
+        N = 256 if N == 768 else N // 2
+    while E * N * K > 48 * 2 ** 20 and K > 256:
+        K //= 2
+    mode = rng.integers(0, 3)   # few rows, tens of rows, or a mix with large groups
+    hi = {0: 4, 1: 70, 2: 300}[int(mode)]
+    sizes = [0 if rng.random() < 0.25 else int(rng.integers(1, hi + 1)) for _ in range(E)]
+    while sum(sizes) * N * K > 600 * 2 ** 20:
+        sizes = [v // 2 for v in sizes]
+    return sizes, K, N, bool(rng.random() < 0.6)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_gemm_random_shapes(seed):
+    """Seeded random shapes through the packed kernels (NONE on even seeds, SWIGLU on odd),
+    and every fourth one on row-major weights as well."""
+    sizes, K, N, gather = _random_gemm_shape(seed)
+    A, Bs, off, A_rows, R = _gemm_case(sizes, K, N, gather, seed=seed)
+    label = f"random seed={seed} E={len(sizes)} R={R} K={K} N={N} gather={gather}"
+    for packed in ([True, False] if seed % 4 == 0 else [True]):
+        if seed % 2 == 0:
+            _run_gemm_none(A, Bs, off, A_rows, R, label, packed)
+        else:
+            _run_gemm_swiglu(A, Bs, off, A_rows, R, label, packed=packed)
+
+
 @pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
 def test_gemm_none_decode_grouped_gemm_full(packed):
     """8 groups x 32 rows, K 6144, N 2048, NONE epilogue -- the single grouped GEMM."""
