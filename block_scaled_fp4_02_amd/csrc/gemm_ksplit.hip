@@ -4,8 +4,9 @@
 // in LDS in a fixed order (deterministic).
 //
 // A workgroup has max(4, KS) waves: NG = waves / KS groups of 64 weight rows, each split
-// over KS waves that take consecutive K ranges.  Chunks hold up to 32 rows (two 16-row
-// token tiles).  Each wave dequantises its own weight and activation fragments into
+// over KS waves that take consecutive K ranges (in the 8-wave workgroup the older wave on
+// each SIMD takes one half step more than its partner: the SIMD issues from it first).
+// Chunks hold up to 32 rows (two 16-row token tiles).  Each wave dequantises its own weight and activation fragments into
 // registers (16x16x32 fp16 MFMA, fragment K order as in gemm_device.hpp).
 //
 // Streaming in half steps: a wave's K range is consumed 128 elements at a time (one of the
@@ -94,8 +95,13 @@ __device__ __forceinline__ float ks_body(const Params &P, float *red, int e, int
   const int g = lane >> 4;        // K group of the lane
   const int I = P.N / 2;
   const int steps = P.K / kKStep;
-  const int iters = steps / KS;
-  const int s_begin = kq * iters;
+  // K range of this wave in half steps: 2 * steps / KS each, except that with one 8-wave
+  // workgroup per CU the first wave on each SIMD (K parts 0-3: the older wave, which the SIMD
+  // issues from first) takes one half step more and its partner one fewer
+  const int base = 2 * steps / KS;
+  const int delta = (KS == 8 && base >= 4) ? 1 : 0;
+  const int halves = base + (kq < KS / 2 ? delta : -delta);
+  const int h_begin = kq * base + (kq < KS / 2 ? kq : KS - kq) * delta;
   // global scales, loaded at the start: left in the epilogue the compiler issues these
   // loads after the last MFMA and waits a full memory round trip for them
   const float gscale = (*P.A_gs) * P.B_gs[e];
@@ -122,19 +128,21 @@ __device__ __forceinline__ float ks_body(const Params &P, float *red, int e, int
     a_code[mt] = static_cast<uint32_t>(src) * half_k + 32 * g;
     a_scale[mt] = static_cast<uint32_t>(src) * k16 + 4 * g;
   }
-  // Half h of the wave's K range: piece q = h % 2 of step s_begin + h / 2.
-  const int halves = 2 * iters;
+  // Half h of the wave's K range is half h_begin + h of the row: piece q = that % 2 of step
+  // that / 2.
   auto load_b = [&](Half16 (&f)[4], int h) {
-    const uint32_t so = h < halves ? static_cast<uint32_t>(s_begin + (h >> 1)) * kPackBlock : kOob;
-    const uint32_t q = static_cast<uint32_t>(h & 1);
+    const int hg = h_begin + h;
+    const uint32_t so = h < halves ? static_cast<uint32_t>(hg >> 1) * kPackBlock : kOob;
+    const uint32_t q = static_cast<uint32_t>(hg & 1);
 #pragma unroll
     for (int j = 0; j < 4; j++)
       load_half16_buf<NT ? kNonTemporal : 0>(f[j], rb, b_code[j] + so + q * 1024, rb, b_scale[j] + so + 2 * q);
   };
   auto load_a = [&](Half16 (&f)[NM], int h) {
     const bool v = h < halves;
-    const uint32_t s = static_cast<uint32_t>(s_begin + (h >> 1));
-    const uint32_t q = static_cast<uint32_t>(h & 1);
+    const int hg = h_begin + h;
+    const uint32_t s = static_cast<uint32_t>(hg >> 1);
+    const uint32_t q = static_cast<uint32_t>(hg & 1);
 #pragma unroll
     for (int mt = 0; mt < NM; mt++)
       load_half16_buf(f[mt], ra_codes, v ? a_code[mt] + s * (kKStep / 2) + 16 * q : kOob, ra_scales,
@@ -173,7 +181,8 @@ __device__ __forceinline__ float ks_body(const Params &P, float *red, int e, int
   Half16 b0[4], b1[4], a0[NM], a1[NM];
   load_b(b0, 0);
   load_a(a0, 0);
-  for (int h = 0; h < halves; h += 2) {   // halves is even
+  int h = 0;
+  for (; h + 2 <= halves; h += 2) {
     load_b(b1, h + 1);
     load_a(a1, h + 1);
     compute(b0, a0);
@@ -181,6 +190,7 @@ __device__ __forceinline__ float ks_body(const Params &P, float *red, int e, int
     load_a(a0, h + 2);
     compute(b1, a1);
   }
+  if (h < halves) compute(b0, a0);   // an odd count: b0 holds the last half
 
   // every wave parks its partial tile; the row group's KS waves then share the units
   float *mine = red + (kq * NG + ng) * kSplitTile;

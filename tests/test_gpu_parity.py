@@ -212,6 +212,7 @@ def _run_gemm_none(A, Bs, off, A_rows, R, label, packed=False):
     ([7, 25], 1024, 512, False),                          # K split 4 ways
     ([45, 3], 2048, 256, True),                           # K split 8 ways, 32 + 13 row chunks
     ([33] * 14, 2048, 2048, True),                        # K split 8 ways: 896 items looped over 256 workgroups
+    ([20, 7, 32], 4096, 256, True),                       # K split 8 ways, 5 and 3 half steps per wave
     ([33] * 32, 512, 2048, False),                        # K split 2 ways: 1024 items looped over 512 workgroups
     ([1] * 60 + [0, 40, 2] + [1] * 37, 2048, 256, True),  # 100 experts, K split 8 ways: listed items looped
     ([0, 1, 2, 3, 5, 8, 13] * 150 + [40, 0], 256, 256, True),  # 1052 experts: two scan blocks in the schedule
@@ -358,7 +359,8 @@ def _run_gemm_swiglu(A, Bs, off, A_rows, R, label, rows=None, packed=False):
                                        ([40] * 256 + [3, 0, 64], 256, 512),
                                        ([0, 130, 255, 97], 768, 256),    # several chunks, odd K steps
                                        ([20, 32], 2048, 256),            # K split 8 ways
-                                       ([33] * 14, 2048, 1024)])         # K split 8 ways, items looped
+                                       ([33] * 14, 2048, 1024),          # K split 8 ways, items looped
+                                       ([20, 32], 6144, 256)])           # K split 8 ways, 7 and 5 half steps
 def test_gemm_swiglu_shapes(sizes, K, I, packed):
     A, Bs, off, A_rows, R = _gemm_case(sizes, K, 2 * I, True, seed=7 + K + I)
     _run_gemm_swiglu(A, Bs, off, A_rows, R, f"sizes={sizes}", packed=packed)
