@@ -40,6 +40,7 @@ struct Params {
   int chunk_rows, n_tiles;
   uint8_t *D_sf;        // SwiGLU + NVFP4 epilogue: scales of D, and the static global scale
   const float *D_gs;
+  int nt_per_item;      // 256-row n tiles per work item (four-wave LDS kernel, one K step)
 };
 
 // Largest expert count for which waves derive their work item from the offsets themselves

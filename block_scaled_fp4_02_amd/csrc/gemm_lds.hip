@@ -244,6 +244,124 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
   }
 }
 
+// One K step (K = 256) and P.nt_per_item consecutive 256-row n tiles per item, NONE epilogue:
+// the chunk's activation tiles are dequantised into LDS once and serve every n tile, and each
+// n tile's weights load while the previous one computes.  With a single K step the start of
+// an item (item lookup, row indices, activation loads and dequantisation, a barrier) costs
+// about as much as its MFMAs, so it is paid once per several n tiles.
+template <int NM, bool NT>
+__device__ __forceinline__ void lds_k1_body(const Params &P, LdsShared<kChunkTiles, 4> &sh, int e, int row0,
+                                            int nrows, int nt_item) {
+  constexpr int WAVES = 4;
+  constexpr int TPW = (kChunkTiles + WAVES - 1) / WAVES;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int ntpi = P.nt_per_item;
+  const int col0 = nt_item * ntpi * 256 + wv * 64;   // first weight row of the wave in n tile 0
+  const uint32_t expert_bytes = static_cast<uint32_t>(P.N / 16) * kPackBlock;   // one K step
+  const BufRsrc rb = make_rsrc(P.B + static_cast<int64_t>(e) * expert_bytes, expert_bytes);
+
+  const uint32_t half_k = P.K / 2, k16 = P.K / 16;
+  const BufRsrc ra_codes = make_rsrc(P.A, static_cast<uint32_t>(P.rows_A * half_k));
+  const BufRsrc ra_scales = make_rsrc(P.A_sf, static_cast<uint32_t>(P.rows_A * k16));
+  Frag16 ra[TPW];
+  bool a_tile[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; i++) {
+    const int t = wv + WAVES * i;
+    a_tile[i] = t < NM;
+    uint32_t code = kOob, scale = kOob;
+    if (a_tile[i]) {
+      const int m = t * 16 + r;
+      int64_t p = row0 + (m < nrows ? m : 0);
+      int64_t src = P.A_rows ? static_cast<int64_t>(P.A_rows[p]) : p;
+      src = src < 0 ? 0 : (src >= P.rows_A ? P.rows_A - 1 : src);
+      code = static_cast<uint32_t>(src) * half_k + 32 * g;
+      scale = static_cast<uint32_t>(src) * k16 + 4 * g;
+    }
+    load_frag16_buf(ra[i], ra_codes, code, 16, ra_scales, scale);
+  }
+  // weights of n tile t (past the item's last n tile: out of range, zeros)
+  auto load_b = [&](Frag16 (&f)[4], int t) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint32_t blk = t < ntpi ? static_cast<uint32_t>((col0 + t * 256 + j * 16) / 16) * kPackBlock : kOob;
+      load_frag16_buf<NT ? kNonTemporal : 0>(f[j], rb, blk + lane * 16, 1024, rb, blk + 2048 + lane * 4);
+    }
+  };
+  Frag16 f0[4], f1[4];
+  load_b(f0, 0);
+#pragma unroll
+  for (int i = 0; i < TPW; i++) {
+    if (!a_tile[i]) continue;
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const half2v sc = e4m3x2_to_f16(ra[i].s, q == 1);
+#pragma unroll
+      for (int d = 0; d < 4; d++)
+        sh.a[0][wv + WAVES * i][4 * q + d][lane] = __builtin_bit_cast(uint4, dequant8(word(ra[i].q[q], d), sc[d >> 1]));
+    }
+  }
+  __syncthreads();
+  const float gscale = (*P.A_gs) * P.B_gs[e];
+
+  auto compute_store = [&](const Frag16 (&fb)[4], int t) {
+    // the activation fragments read below are the same for every n tile: without this
+    // compiler-only memory clobber their 8 * NM LDS reads are hoisted out of the loop and
+    // held in registers (spills at 168 VGPRs); it emits no instruction
+    asm volatile("" ::: "memory");
+    float4v acc[4][NM];
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int mt = 0; mt < NM; mt++) acc[j][mt] = float4v{};
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      half2v bsc[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) bsc[j] = e4m3x2_to_f16(fb[j].s, q == 1);
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        half8 af[NM];
+#pragma unroll
+        for (int mt = 0; mt < NM; mt++) af[mt] = __builtin_bit_cast(half8, sh.a[0][mt][4 * q + d][lane]);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const half8 bf = dequant8(word(fb[j].q[q], d), bsc[j][d >> 1]);
+#pragma unroll
+          for (int mt = 0; mt < NM; mt++)
+            acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[mt], acc[j][mt], 0, 0, 0);
+        }
+      }
+    }
+    // 16x16 D lane layout: weight row 4g + i of tile j, token row r of tile mt
+#pragma unroll
+    for (int mt = 0; mt < NM; mt++) {
+      const int m = mt * 16 + r;
+      if (m < nrows) {
+        uint16_t *drow = static_cast<uint16_t *>(P.D) + (row0 + m) * static_cast<int64_t>(P.N);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const uint32_t lo = f32_to_bf16(acc[j][mt][0] * gscale) |
+                              (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][1] * gscale)) << 16);
+          const uint32_t hi = f32_to_bf16(acc[j][mt][2] * gscale) |
+                              (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][3] * gscale)) << 16);
+          *reinterpret_cast<uint2 *>(drow + col0 + t * 256 + j * 16 + 4 * g) = make_uint2(lo, hi);
+        }
+      }
+    }
+  };
+#pragma unroll 1
+  for (int t = 0; t < ntpi; t += 2) {
+    load_b(f1, t + 1);
+    compute_store(f0, t);
+    load_b(f0, t + 2);
+    if (t + 1 < ntpi) compute_store(f1, t + 1);
+  }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(256, 3) void gemm_lds_kernel(Params P) {
   __shared__ LdsShared<kChunkTiles, 4> sh;
@@ -255,6 +373,20 @@ __global__ __launch_bounds__(256, 3) void gemm_lds_kernel(Params P) {
     return;
   }
   const int nm = (item.z + 15) / 16;   // workgroup-uniform
+  if constexpr (EPI == MOE_EPI_NONE) {
+    if (P.nt_per_item > 1) {   // one K step, several n tiles per item
+      if (last) {
+        if (nm <= 1) lds_k1_body<1, true>(P, sh, item.x, item.y, item.z, item.w);
+        else if (nm == 2) lds_k1_body<2, true>(P, sh, item.x, item.y, item.z, item.w);
+        else lds_k1_body<3, true>(P, sh, item.x, item.y, item.z, item.w);
+      } else {
+        if (nm <= 1) lds_k1_body<1, false>(P, sh, item.x, item.y, item.z, item.w);
+        else if (nm == 2) lds_k1_body<2, false>(P, sh, item.x, item.y, item.z, item.w);
+        else lds_k1_body<3, false>(P, sh, item.x, item.y, item.z, item.w);
+      }
+      return;
+    }
+  }
   if (last) {   // the expert's last chunk: no later item re-reads these weights
     if (nm <= 1) lds_body<1, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
     else if (nm == 2) lds_body<2, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);

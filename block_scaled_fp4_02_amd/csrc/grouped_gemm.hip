@@ -158,6 +158,16 @@ GemmPlan plan_gemm(const moe_gemm_args &a) {
       p.kernel = kLdsWide;
       p.chunk_rows = kWideChunkTiles * 16;
       p.n_tile = 512;
+    } else if (a.K == kKStep && a.epilogue == MOE_EPI_NONE) {
+      // one K step per item: several 256-row n tiles per item reuse the activation tile the
+      // workgroup dequantised into LDS (the item's start-up -- lookup, row indices, activation
+      // loads, barrier -- otherwise dominates); keep about three items per workgroup slot
+      for (const int m : {4, 3, 2}) {
+        if ((a.N / 256) % m == 0 && chunk_estimate(a, p.chunk_rows) * (a.N / 256 / m) >= 3 * 768) {
+          p.n_tile = 256 * m;
+          break;
+        }
+      }
     } else if (chunk_estimate(a, p.chunk_rows) * (a.N / 256) * 4 < kFullChip) {
       // few items: split K across the waves of a workgroup (2, 4 or 8 ways)
       const int chunk = ksplit_chunk_rows();
@@ -211,7 +221,7 @@ hipError_t launch_grouped_gemm(const moe_gemm_args &a, const GemmPlan &plan, voi
   }
   const Params p{a.A, a.A_sf, a.A_gs, a.A_rows, a.rows_A, a.B, a.B_sf, a.B_gs, a.E, a.N, a.K,
                  a.D, a.amax_out, items, count, a.expert_offsets, a.R, plan.chunk_rows, plan.n_tiles,
-                 a.D_sf, a.D_gs};
+                 a.D_sf, a.D_gs, plan.kernel == kLds ? plan.n_tile / 256 : 1};
   const dim3 grid(static_cast<uint32_t>(plan.grid));
   switch (plan.kernel) {
     case kLds: launch_lds(p, a.epilogue, grid, stream); break;
