@@ -133,6 +133,18 @@ def test_ksplit_grid_is_capped_at_resident_workgroups():
     assert slots(E=256, N=4096, K=6144, R=8192) == (8192 // 48 + 1 + 256) * 16
 
 
+def test_single_step_items_cover_several_n_tiles():
+    """K = 256 (one K step) with the NONE epilogue: each item of the four-wave kernel covers
+    several 256-row n tiles, as many as keep about three items per workgroup slot (2 at the
+    TP8 share's down GEMM: 256 experts, 8192 rows, N 6144); SWIGLU and longer K keep one."""
+    L = moe.lib()
+    slots = lambda **kw: L.moe_grouped_gemm_nvfp4_amax_slots(C.byref(gemm_args(layout=1, **kw)))
+    bound_items = lambda n_tiles: -(-((8192 + 47) // 48 + 256) * n_tiles // 8) * 8
+    assert slots(E=256, N=6144, K=256, R=8192) == bound_items(12)
+    assert slots(E=256, N=6144, K=256, R=8192, epi=1) == bound_items(24)
+    assert slots(E=256, N=6144, K=512, R=8192) == bound_items(24)
+
+
 def test_gemm_workspace_grows_with_rows_and_experts():
     L = moe.lib()
     small = L.moe_grouped_gemm_nvfp4_workspace(C.byref(gemm_args(E=8, R=256)))
