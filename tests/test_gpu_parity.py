@@ -252,6 +252,16 @@ def _random_gemm_shape(seed):
     return sizes, K, N, bool(rng.random() < 0.6)
 
 
+def test_gemm_none_single_k_step_several_n_tiles():
+    """K = 256 with the NONE epilogue and enough items: each work item of the four-wave kernel
+    covers two 256-row n tiles that share one dequantised activation tile (192 experts,
+    ragged and empty groups, gathered rows, N 6144)."""
+    rng = np.random.default_rng(4242)
+    sizes = [0 if rng.random() < 0.1 else int(rng.integers(1, 61)) for _ in range(192)]
+    A, Bs, off, A_rows, R = _gemm_case(sizes, 256, 6144, True, seed=4242)
+    _run_gemm_none(A, Bs, off, A_rows, R, "single K step, two n tiles per item", True)
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_gemm_random_shapes(seed):
     """Seeded random shapes through the packed kernels (NONE on even seeds, SWIGLU on odd),
