@@ -35,9 +35,17 @@ namespace moe {
 namespace gemm {
 namespace {
 
+// Row of the NONE epilogue's staging area: a wave's 64 bf16 output columns of one token row
+// (128 B) plus 16 B of padding, so that the 16 rows a store instruction of the MFMA layout
+// touches fall in different LDS banks and every row starts 16-byte aligned.
+constexpr int kEpRow = 72;
+
 template <int MAXT, int WAVES>
 struct LdsShared {
-  uint4 a[2][MAXT][8][64];   // [buffer][token tile][MFMA of step][lane]
+  union {
+    uint4 a[2][MAXT][8][64];                  // [buffer][token tile][MFMA of step][lane]
+    uint16_t ep[WAVES][MAXT * 16][kEpRow];    // NONE epilogue: [wave][token row][column]
+  };
   float wmax[WAVES];
 };
 
@@ -200,35 +208,51 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
     }
     return;
   }
+  if constexpr (EPI == MOE_EPI_NONE) {
+    // Stage the wave's bf16 tile in LDS in row order, then store whole 128-byte row pieces:
+    // in the MFMA layout a lane holds 4 consecutive columns of one row, so each store
+    // instruction would write 16 separate 32-byte pieces of 16 rows.  (The last K step ended
+    // with a barrier, so the activation buffers that share this space are free.)
+    uint16_t(*ep)[kEpRow] = sh.ep[wv];
+#pragma unroll
+    for (int mt = 0; mt < NM; mt++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const uint32_t lo = f32_to_bf16(acc[j][mt][0] * gscale) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][1] * gscale)) << 16);
+        const uint32_t hi = f32_to_bf16(acc[j][mt][2] * gscale) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][3] * gscale)) << 16);
+        *reinterpret_cast<uint2 *>(&ep[mt * 16 + r][j * 16 + 4 * g]) = make_uint2(lo, hi);
+      }
+    __syncthreads();
+    const int c = lane & 7;    // 16-byte piece of the row
+    const int col = nrow[0] + 8 * c;   // the wave's 64 columns start at nrow[0]
+#pragma unroll
+    for (int k = 0; k < 2 * NM; k++) {
+      const int m = 8 * k + (lane >> 3);
+      const uint4 v = *reinterpret_cast<const uint4 *>(&ep[m][8 * c]);
+      if (m < nrows)
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(P.D) + (row0 + m) * static_cast<int64_t>(P.N) + col) = v;
+    }
+    return;
+  }
+  // SWIGLU: act columns nrow[jp] + 4g .. + 3 of token row m
   float amax = 0.f;
 #pragma unroll
   for (int mt = 0; mt < NM; mt++) {
     const int m = mt * 16 + r;
     if (m < nrows) {
-      const int64_t p = row0 + m;
-      if (EPI == MOE_EPI_NONE) {
-        uint16_t *drow = static_cast<uint16_t *>(P.D) + p * P.N;
+      uint16_t *drow = static_cast<uint16_t *>(P.D) + (row0 + m) * static_cast<int64_t>(I);
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const uint32_t lo = f32_to_bf16(acc[j][mt][0] * gscale) |
-                              (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][1] * gscale)) << 16);
-          const uint32_t hi = f32_to_bf16(acc[j][mt][2] * gscale) |
-                              (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][3] * gscale)) << 16);
-          *reinterpret_cast<uint2 *>(drow + nrow[j] + 4 * g) = make_uint2(lo, hi);
+      for (int jp = 0; jp < 2; jp++) {
+        uint16_t o[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          o[c] = swiglu_bf16(acc[jp][mt][c] * gscale, acc[2 + jp][mt][c] * gscale);
+          amax = fmaxf(amax, fabsf(bf16_to_f32(o[c])));
         }
-      } else {
-        uint16_t *drow = static_cast<uint16_t *>(P.D) + p * I;
-#pragma unroll
-        for (int jp = 0; jp < 2; jp++) {
-          uint16_t o[4];
-#pragma unroll
-          for (int c = 0; c < 4; c++) {
-            o[c] = swiglu_bf16(acc[jp][mt][c] * gscale, acc[2 + jp][mt][c] * gscale);
-            amax = fmaxf(amax, fabsf(bf16_to_f32(o[c])));
-          }
-          *reinterpret_cast<uint2 *>(drow + nrow[jp] + 4 * g) =
-              make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
-        }
+        *reinterpret_cast<uint2 *>(drow + nrow[jp] + 4 * g) =
+            make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
       }
     }
   }
