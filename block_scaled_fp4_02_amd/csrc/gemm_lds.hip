@@ -93,19 +93,29 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
   const BufRsrc ra_scales = make_rsrc(P.A_sf, static_cast<uint32_t>(P.rows_A * k16));
   bool a_tile[TPW];
   uint32_t a_code[TPW], a_scale[TPW];
+  // token rows: the row-index loads of all tiles are issued before any is used (each index
+  // is a row of the item, so no branch is needed around them)
+  int64_t src_row[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; i++) {
     const int t = wv + AW * i;
     a_tile[i] = wv < AW && t < NM;
-    a_code[i] = a_scale[i] = 0;
-    if (a_tile[i]) {
-      const int m = t * 16 + r;
-      int64_t p = row0 + (m < nrows ? m : 0);
-      int64_t src = P.A_rows ? static_cast<int64_t>(P.A_rows[p]) : p;
-      src = src < 0 ? 0 : (src >= P.rows_A ? P.rows_A - 1 : src);
-      a_code[i] = static_cast<uint32_t>(src) * half_k + 32 * g;
-      a_scale[i] = static_cast<uint32_t>(src) * k16 + 4 * g;
-    }
+    const int m = t * 16 + r;
+    src_row[i] = row0 + (m < nrows ? m : 0);
+  }
+  if (P.A_rows) {
+    int32_t idx[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; i++) idx[i] = P.A_rows[src_row[i]];
+#pragma unroll
+    for (int i = 0; i < TPW; i++) src_row[i] = idx[i];
+  }
+#pragma unroll
+  for (int i = 0; i < TPW; i++) {
+    int64_t src = src_row[i];
+    src = src < 0 ? 0 : (src >= P.rows_A ? P.rows_A - 1 : src);
+    a_code[i] = a_tile[i] ? static_cast<uint32_t>(src) * half_k + 32 * g : 0;
+    a_scale[i] = a_tile[i] ? static_cast<uint32_t>(src) * k16 + 4 * g : 0;
   }
   auto load_a = [&](Frag16 (&f)[TPW], int s) {
 #pragma unroll
@@ -150,6 +160,9 @@ __device__ __forceinline__ void lds_body(const Params &P, LdsShared<MAXT, WAVES>
   // loads in the same order.
   Frag16 f0[4], f1[4], ra[TPW], ra0[TPW];
   load_a(ra0, 0);
+  // keep the first activation tiles' loads ahead of the weight loads, so that their
+  // dequantisation below waits for them alone
+  __builtin_amdgcn_sched_barrier(0);
   load_a(ra, 1);
   load_b(f0, 0);
   store_a(ra0, 0);

@@ -32,4 +32,32 @@ __device__ __forceinline__ uint32_t e2m1_rne(float u) {
   return (b >> 22) - (126u << 1);
 }
 
+// Correctly rounded binary32 quotients a / b of one block by one divisor b = s * g, from a
+// single correctly rounded reciprocal y = 1 / b: q = a * y is within one ulp of a / b, the
+// remainder r = a - q * b is exact as one fma, and q + r * y rounded once is the correctly
+// rounded quotient (Markstein's theorem on division by fused multiply-add; Muller et al.,
+// Handbook of Floating-Point Arithmetic, the chapter on algorithms using the fma).  The
+// theorem needs every step clear of underflow and overflow, so the form applies only when
+// b lies well inside the normal range and the block maximum over b stays far below
+// overflow; otherwise (`fast` false, which covers b = 0) the caller divides each element.
+// Quotients small enough to underflow round to the E2M1 code 0 either way.
+struct BlockDivisor {
+  float b, y;
+  bool fast;
+};
+
+__device__ __forceinline__ BlockDivisor block_divisor(float b, float amax) {
+  BlockDivisor d;
+  d.b = b;
+  d.y = 1.0f / b;
+  d.fast = b >= 0x1p-100f && b <= 0x1p100f && amax * d.y < 0x1p100f;
+  return d;
+}
+
+__device__ __forceinline__ float block_quotient(float a, const BlockDivisor &d) {
+  const float q = a * d.y;
+  const float r = __builtin_fmaf(-q, d.b, a);
+  return __builtin_fmaf(r, d.y, q);
+}
+
 }  // namespace moe

@@ -7,7 +7,9 @@
 // all-zero tensor); block scale s = e4m3_rne(min(amax_b / (6 g), 448)); element code
 // sign(x) | e2m1_rne(min(|x| / (s g), 6)).  Every step is one correctly rounded binary32
 // operation in a fixed order, so the result is bit-exact against any implementation that
-// takes the same steps.  Contraction is disabled in this file for that reason.
+// takes the same steps.  Contraction is disabled in this file for that reason; the
+// element quotients come from one reciprocal per block with an exact fma correction, which
+// yields the correctly rounded quotient itself (block_quotient).
 //
 // Two kernels: amax_kernel writes up to kAmaxParts partial maxima into the workspace;
 // quant_kernel (one thread per 16-element block) first reduces those partials itself
@@ -144,12 +146,20 @@ __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, 
   const float t = fminf(amax_b / six_g, 448.0f);
   const uint32_t s = e4m3_rne(t);
   const float sg = e4m3_value(s) * g;
+  uint32_t mag[16];
+  const BlockDivisor d = block_divisor(sg, amax_b);
+  if (d.fast) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) mag[i] = e2m1_rne(fminf(block_quotient(fabsf(v[i]), d), 6.0f));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; i++) mag[i] = (s != 0u) ? e2m1_rne(fminf(fabsf(v[i]) / sg, 6.0f)) : 0u;
+  }
   uint32_t packed[2] = {0u, 0u};
 #pragma unroll
   for (int i = 0; i < 16; i++) {
     const uint32_t sign = (__float_as_uint(v[i]) >> 31) << 3;
-    const uint32_t mag = (s != 0u) ? e2m1_rne(fminf(fabsf(v[i]) / sg, 6.0f)) : 0u;
-    packed[i >> 3] |= (sign | mag) << (4 * (i & 7));
+    packed[i >> 3] |= (sign | mag[i]) << (4 * (i & 7));
   }
   reinterpret_cast<uint2 *>(q)[b] = make_uint2(packed[0], packed[1]);
   sf[b] = static_cast<uint8_t>(s);

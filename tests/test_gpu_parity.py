@@ -166,6 +166,30 @@ def test_quantize_edges(case):
     _check_quant(x, bf16=False)
 
 
+def test_quantize_rounding_thresholds():
+    """Element quotients |x| / (s g) exactly on, and within 4 ulps of, every E2M1 rounding
+    threshold and grid value, for block scales across the E4M3 range (static g).  The first
+    element of each block fixes the block maximum at 6 s g."""
+    g = np.float32(0.0123)
+    six_g = np.float32(np.float32(6.0) * g)
+    svals = np.array([6 * 2.0 ** -9, 0.375, 1.0, 2.5, 13.0, 104.0, 448.0], np.float32)
+    targets = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, 0.125],
+                       np.float32)
+    blocks = []
+    for sv in svals:
+        sg = np.float32(sv * g)
+        amax = np.float32(sv * six_g)
+        for k in range(-4, 5):
+            vals = (targets * sg).astype(np.float32)
+            vals = (vals.view(np.int32) + np.int32(k)).view(np.float32)
+            vals = np.minimum(vals, amax)
+            blk = np.concatenate([[amax], vals]).astype(np.float32)
+            blk[1::2] *= -1
+            blocks.append(blk)
+    x = np.stack(blocks).reshape(len(svals), -1)
+    _check_quant(x, bf16=False, g=float(g))
+
+
 # ---------------------------------------------------------------------------------------
 # grouped GEMM, NONE epilogue
 
