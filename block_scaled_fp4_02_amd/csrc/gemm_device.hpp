@@ -255,21 +255,19 @@ __device__ __forceinline__ void swiglu_nvfp4_block(const float4v &gate, const fl
   const float t = fminf(amax / six_g, 448.0f);
   const uint32_t s = e4m3_rne(t);
   const float sg = e4m3_value(s) * g2;
-  uint32_t mag[4];
+  uint32_t packed = 0u;
   const BlockDivisor d = block_divisor(sg, amax);
   if (d.fast) {
+    float u[4];
 #pragma unroll
-    for (int c = 0; c < 4; c++) mag[c] = e2m1_rne(fminf(block_quotient(fabsf(v[c]), d), 6.0f));
+    for (int c = 0; c < 4; c++) u[c] = block_quotient(fabsf(v[c]), d);
+    packed = e2m1_pack4(u);
   } else {
 #pragma unroll
-    for (int c = 0; c < 4; c++) mag[c] = (s != 0u) ? e2m1_rne(fminf(fabsf(v[c]) / sg, 6.0f)) : 0u;
+    for (int c = 0; c < 4; c++) packed |= ((s != 0u) ? e2m1_rne(fminf(fabsf(v[c]) / sg, 6.0f)) : 0u) << (4 * c);
   }
-  uint32_t packed = 0u;
 #pragma unroll
-  for (int c = 0; c < 4; c++) {
-    const uint32_t sign = (__float_as_uint(v[c]) >> 31) << 3;
-    packed |= (sign | mag[c]) << (4 * c);
-  }
+  for (int c = 0; c < 4; c++) packed |= (__float_as_uint(v[c]) >> 31) << (4 * c + 3);
   if (store) {
     *reinterpret_cast<uint16_t *>(codes + 2 * g) = static_cast<uint16_t>(packed);
     if (g == 0) *scale = static_cast<uint8_t>(s);

@@ -60,4 +60,24 @@ __device__ __forceinline__ float block_quotient(float a, const BlockDivisor &d) 
   return __builtin_fmaf(r, d.y, q);
 }
 
+// E2M1 codes of eight non-negative binary32 values, two per hardware conversion, packed
+// low nibble first.  With a unit scale the conversion rounds to nearest even and saturates
+// at 6, and equals e2m1_rne(min(u, 6)) for every non-negative binary32 u (every such bit
+// pattern, +inf included, checked on gfx950).
+__device__ __forceinline__ uint32_t e2m1_pack8(const float (&u)[8]) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, u[0], u[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, u[2], u[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, u[4], u[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, u[6], u[7], 1.0f, 3);
+  return w;
+}
+
+__device__ __forceinline__ uint32_t e2m1_pack4(const float (&u)[4]) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, u[0], u[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, u[2], u[3], 1.0f, 1);
+  return w;
+}
+
 }  // namespace moe

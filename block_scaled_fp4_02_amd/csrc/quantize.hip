@@ -146,21 +146,26 @@ __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, 
   const float t = fminf(amax_b / six_g, 448.0f);
   const uint32_t s = e4m3_rne(t);
   const float sg = e4m3_value(s) * g;
-  uint32_t mag[16];
+  uint32_t packed[2] = {0u, 0u};
   const BlockDivisor d = block_divisor(sg, amax_b);
   if (d.fast) {
+    // finite quotients: the hardware conversion saturates at 6 itself
 #pragma unroll
-    for (int i = 0; i < 16; i++) mag[i] = e2m1_rne(fminf(block_quotient(fabsf(v[i]), d), 6.0f));
+    for (int h = 0; h < 2; h++) {
+      float u[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) u[i] = block_quotient(fabsf(v[8 * h + i]), d);
+      packed[h] = e2m1_pack8(u);
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; i++) mag[i] = (s != 0u) ? e2m1_rne(fminf(fabsf(v[i]) / sg, 6.0f)) : 0u;
+    for (int i = 0; i < 16; i++) {
+      const uint32_t mag = (s != 0u) ? e2m1_rne(fminf(fabsf(v[i]) / sg, 6.0f)) : 0u;
+      packed[i >> 3] |= mag << (4 * (i & 7));
+    }
   }
-  uint32_t packed[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const uint32_t sign = (__float_as_uint(v[i]) >> 31) << 3;
-    packed[i >> 3] |= (sign | mag[i]) << (4 * (i & 7));
-  }
+  for (int i = 0; i < 16; i++) packed[i >> 3] |= (__float_as_uint(v[i]) >> 31) << (4 * (i & 7) + 3);
   reinterpret_cast<uint2 *>(q)[b] = make_uint2(packed[0], packed[1]);
   sf[b] = static_cast<uint8_t>(s);
 }
