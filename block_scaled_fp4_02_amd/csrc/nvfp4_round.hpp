@@ -33,9 +33,11 @@ __device__ __forceinline__ uint32_t e2m1_rne(float u) {
 }
 
 // Correctly rounded binary32 quotients a / b of one block by one divisor b = s * g, from a
-// single correctly rounded reciprocal y = 1 / b: q = a * y is within one ulp of a / b, the
-// remainder r = a - q * b is exact as one fma, and q + r * y rounded once is the correctly
-// rounded quotient (Markstein's theorem on division by fused multiply-add; Muller et al.,
+// single correctly rounded reciprocal y = 1 / b and fma corrections.  q0 = a * y can be a
+// little more than one ulp from a / b; one correction q1 = q0 + (a - q0 b) y makes it
+// faithful (within one ulp), the remainder r1 = a - q1 b is then exact as one fma, and
+// q1 + r1 y rounded once is the correctly rounded quotient (Markstein's theorem on division
+// by fused multiply-add, which needs y correctly rounded and q1 faithful; Muller et al.,
 // Handbook of Floating-Point Arithmetic, the chapter on algorithms using the fma).  The
 // theorem needs every step clear of underflow and overflow, so the form applies only when
 // b lies well inside the normal range and the block maximum over b stays far below
@@ -55,9 +57,11 @@ __device__ __forceinline__ BlockDivisor block_divisor(float b, float amax) {
 }
 
 __device__ __forceinline__ float block_quotient(float a, const BlockDivisor &d) {
-  const float q = a * d.y;
-  const float r = __builtin_fmaf(-q, d.b, a);
-  return __builtin_fmaf(r, d.y, q);
+  const float q0 = a * d.y;
+  const float r0 = __builtin_fmaf(-q0, d.b, a);
+  const float q1 = __builtin_fmaf(r0, d.y, q0);  // faithful
+  const float r1 = __builtin_fmaf(-q1, d.b, a);  // exact
+  return __builtin_fmaf(r1, d.y, q1);
 }
 
 // E2M1 codes of eight non-negative binary32 values, two per hardware conversion, packed
