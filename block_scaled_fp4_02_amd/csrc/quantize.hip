@@ -95,6 +95,21 @@ __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, 
                                                     uint8_t *__restrict__ sf, float *__restrict__ gs,
                                                     int dynamic, const float *__restrict__ parts,
                                                     int nparts) {
+  // the block's loads go out first, so their latency overlaps the global-scale reduction
+  // and the barrier (a thread past the end loads the last block and drops it)
+  const int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t bl = b < nblk ? b : nblk - 1;
+  const bool bf16 = x_dtype == MOE_DTYPE_BF16;
+  uint4 raw[4] = {};
+  if (nblk > 0) {
+    const uint4 *xv = static_cast<const uint4 *>(x) + (bf16 ? 2 : 4) * bl;
+    raw[0] = xv[0];
+    raw[1] = xv[1];
+    if (!bf16) {
+      raw[2] = xv[2];
+      raw[3] = xv[3];
+    }
+  }
   __shared__ float sh_g;
   if (threadIdx.x < 64) {
     float g;
@@ -116,27 +131,22 @@ __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, 
   }
   __syncthreads();
   const float g = sh_g;
-  const int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (b >= nblk) return;
   float v[16];
-  if (x_dtype == MOE_DTYPE_BF16) {
-    const uint4 *xv = static_cast<const uint4 *>(x) + 2 * b;
-    const uint4 a = xv[0], c = xv[1];
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+  if (bf16) {
+    const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       v[2 * i] = __uint_as_float(w[i] << 16);
       v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   } else {
-    const float4 *xv = static_cast<const float4 *>(x) + 4 * b;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const float4 f = xv[i];
-      v[4 * i] = f.x;
-      v[4 * i + 1] = f.y;
-      v[4 * i + 2] = f.z;
-      v[4 * i + 3] = f.w;
+      v[4 * i] = __uint_as_float(raw[i].x);
+      v[4 * i + 1] = __uint_as_float(raw[i].y);
+      v[4 * i + 2] = __uint_as_float(raw[i].z);
+      v[4 * i + 3] = __uint_as_float(raw[i].w);
     }
   }
   float amax_b = 0.f;
