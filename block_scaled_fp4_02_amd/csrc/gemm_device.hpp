@@ -11,6 +11,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "lds_budget.hpp"
 #include "nvfp4_round.hpp"
 
 namespace moe {
@@ -252,7 +253,7 @@ __device__ __forceinline__ void swiglu_nvfp4_block(const float4v &gate, const fl
   amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
   amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
   const float six_g = 6.0f * g2;
-  const float t = fminf(amax / six_g, 448.0f);
+  const float t = amax > 0.f ? fminf(amax / six_g, 448.0f) : 0.f;   // 0 / 0 counts as 0
   const uint32_t s = e4m3_rne(t);
   const float sg = e4m3_value(s) * g2;
   uint32_t packed = 0u;
@@ -264,7 +265,8 @@ __device__ __forceinline__ void swiglu_nvfp4_block(const float4v &gate, const fl
     packed = e2m1_pack4(u);
   } else {
 #pragma unroll
-    for (int c = 0; c < 4; c++) packed |= ((s != 0u) ? e2m1_rne(fminf(fabsf(v[c]) / sg, 6.0f)) : 0u) << (4 * c);
+    for (int c = 0; c < 4; c++)
+      packed |= ((s != 0u && fabsf(v[c]) > 0.f) ? e2m1_rne(fminf(fabsf(v[c]) / sg, 6.0f)) : 0u) << (4 * c);
   }
 #pragma unroll
   for (int c = 0; c < 4; c++) packed |= (__float_as_uint(v[c]) >> 31) << (4 * c + 3);

@@ -251,6 +251,10 @@ __global__ __launch_bounds__(64 * split_waves<KS>(), 8 / split_waves<KS>()) void
   constexpr int WAVES = split_waves<KS>();
   __shared__ float red[WAVES * kSplitTile];
   __shared__ float wmax[WAVES];
+  static_assert(sizeof(red) + sizeof(wmax) == lds::ksplit_kernel_bytes(kSplitTiles, WAVES),
+                "LDS of the K-split kernel differs from its budget entry");
+  static_assert(lds::fits_cu(lds::ksplit_kernel_bytes(kSplitTiles, WAVES), 8 / WAVES),
+                "K-split tile exceeds the CU's LDS");
   float amax = 0.f;
   for (int vb = blockIdx.x;; vb += gridDim.x) {   // a multiple of 8 apart: the same XCD
     int4 item;

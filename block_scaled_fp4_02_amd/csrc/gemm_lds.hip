@@ -22,7 +22,7 @@
 //  * In the four-wave kernel the expert's last row chunk loads its weights with the
 //    non-temporal hint (no later item of the launch reads them again); earlier chunks keep
 //    them in L2 for the next chunk.
-// Chunks of up to 48 rows (three token tiles), 48 KB of LDS and at most 168 VGPRs, so three
+// Chunks of up to 48 rows (three token tiles), 49,168 bytes of LDS and at most 168 VGPRs, so three
 // workgroups share a CU and overlap one another's loads, dequantisation and MFMAs.  Per step
 // and wave: 264 VALU (weight dequantisation) for 32*NM MFMAs.  At decode sizes the kernel
 // streams weights (HBM-bound); at hundreds of rows per expert it runs the same tile over
@@ -39,6 +39,7 @@ namespace {
 // (128 B) plus 16 B of padding, so that the 16 rows a store instruction of the MFMA layout
 // touches fall in different LDS banks and every row starts 16-byte aligned.
 constexpr int kEpRow = 72;
+static_assert(kEpRow == lds::kEpRowHalves, "NONE staging row differs from the LDS budget");
 
 template <int MAXT, int WAVES>
 struct LdsShared {
@@ -399,8 +400,19 @@ __device__ __forceinline__ void lds_k1_body(const Params &P, LdsShared<kChunkTil
   }
 }
 
+// LDS budget (lds_budget.hpp): the shared struct is exactly the budget entry, and the
+// workgroups the launch bounds promise per CU fit in its 160 KB.
+constexpr int kLdsWgPerCu = 3;
+constexpr int kWideWgPerCu = 1;
+static_assert(sizeof(LdsShared<kChunkTiles, 4>) == lds::lds_kernel_bytes(kChunkTiles, 4),
+              "LDS of the four-wave kernel differs from its budget entry");
+static_assert(lds::fits_cu(sizeof(LdsShared<kChunkTiles, 4>), kLdsWgPerCu), "four-wave tile exceeds the CU's LDS");
+static_assert(sizeof(LdsShared<kWideChunkTiles, 8>) == lds::lds_kernel_bytes(kWideChunkTiles, 8),
+              "LDS of the eight-wave kernel differs from its budget entry");
+static_assert(lds::fits_cu(sizeof(LdsShared<kWideChunkTiles, 8>), kWideWgPerCu), "eight-wave tile exceeds the CU's LDS");
+
 template <int EPI>
-__global__ __launch_bounds__(256, 3) void gemm_lds_kernel(Params P) {
+__global__ __launch_bounds__(256, kLdsWgPerCu) void gemm_lds_kernel(Params P) {
   __shared__ LdsShared<kChunkTiles, 4> sh;
   const int b = blockIdx.x;
   int4 item;
@@ -437,10 +449,11 @@ __global__ __launch_bounds__(256, 3) void gemm_lds_kernel(Params P) {
 
 // Hundreds of rows per expert: eight waves share one activation tile of up to six token
 // tiles (96 rows), so each dequantised weight element serves twice as many tokens as in
-// gemm_lds_kernel, while two waves per SIMD (one workgroup of 512 threads per CU, 96 KB of
-// LDS) keep VALU and MFMA issuing side by side.  Token tiles rounded up to an even count.
+// gemm_lds_kernel, while two waves per SIMD (one workgroup of 512 threads per CU, 110,624
+// bytes of LDS: the 96 KB activation buffers share a union with the 108 KB NONE staging
+// area) keep VALU and MFMA issuing side by side.  Token tiles rounded up to an even count.
 template <int EPI>
-__global__ __launch_bounds__(512, 1) void gemm_lds_wide_kernel(Params P) {
+__global__ __launch_bounds__(512, kWideWgPerCu) void gemm_lds_wide_kernel(Params P) {
   __shared__ LdsShared<kWideChunkTiles, 8> sh;
   const int b = blockIdx.x;
   int4 item;

@@ -129,6 +129,7 @@ __device__ __forceinline__ void rm_body(const Params &P, float *red, float *wmax
     }
     __syncthreads();
     if (kq == 0) {
+#pragma unroll 1
       for (int o = 1; o < KS; o++) {
         const float *src = red + ((o - 1) * NG + ng) * TILE;
 #pragma unroll
@@ -189,11 +190,16 @@ __device__ __forceinline__ void rm_body(const Params &P, float *red, float *wmax
   }
 }
 
+constexpr int kRowMajorWgPerCu = 2;   // workgroups per CU the launch bounds promise
+
 template <int KS, int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_rowmajor_kernel(Params P) {
+__global__ __launch_bounds__(256, kRowMajorWgPerCu) void gemm_rowmajor_kernel(Params P) {
   constexpr int TILE = 2 * 2 * 16 * 64;
   __shared__ float red[KS > 1 ? (KS - 1) * (4 / KS) * TILE : 1];
   __shared__ float wmax[4];
+  static_assert(TILE == lds::kRowMajorPartialFloats && sizeof(red) + sizeof(wmax) == lds::rowmajor_kernel_bytes(KS),
+                "LDS of the row-major kernel differs from its budget entry");
+  static_assert(lds::fits_cu(lds::rowmajor_kernel_bytes(KS), kRowMajorWgPerCu), "row-major tile exceeds the CU's LDS");
   const int b = blockIdx.x;
   int4 item;
   if (!item_for_block(P, b, item)) {

@@ -1,7 +1,8 @@
 // NVFP4 rounding steps shared by the quantiser and the fused SwiGLU + NVFP4 GEMM epilogue.
 // Reading of the open steps (format: "Cracking the SM120 Shared Memory Ceiling", section
 // "The Shared Memory Calculation"): block scale s = e4m3_rne(min(amax_b / (6 g), 448)),
-// element code sign(x) | e2m1_rne(min(|x| / (s g), 6)), every step one correctly rounded
+// element code sign(x) | e2m1_rne(min(|x| / (s g), 6)) (0 / 0, a zero block or element over
+// an underflowed g or s g, counts as 0), every step one correctly rounded
 // binary32 operation in this order -- callers compile these with contraction off.
 #pragma once
 

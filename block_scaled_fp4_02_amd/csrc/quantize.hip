@@ -5,7 +5,8 @@
 //
 // Reading of the open steps: decode-direction global scale g = amax / (6 * 448) (1 for an
 // all-zero tensor); block scale s = e4m3_rne(min(amax_b / (6 g), 448)); element code
-// sign(x) | e2m1_rne(min(|x| / (s g), 6)).  Every step is one correctly rounded binary32
+// sign(x) | e2m1_rne(min(|x| / (s g), 6)), where 0 / 0 (a zero block or element over an
+// underflowed g or s g) counts as 0.  Every step is one correctly rounded binary32
 // operation in a fixed order, so the result is bit-exact against any implementation that
 // takes the same steps.  Contraction is disabled in this file for that reason; the
 // element quotients come from one reciprocal per block with an exact fma correction, which
@@ -153,7 +154,8 @@ __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, 
 #pragma unroll
   for (int i = 0; i < 16; i++) amax_b = fmaxf(amax_b, fabsf(v[i]));
   const float six_g = 6.0f * g;
-  const float t = fminf(amax_b / six_g, 448.0f);
+  // zero stays zero where g has underflowed: a zero block gets scale 0 (not 0 / 0)
+  const float t = amax_b > 0.f ? fminf(amax_b / six_g, 448.0f) : 0.f;
   const uint32_t s = e4m3_rne(t);
   const float sg = e4m3_value(s) * g;
   uint32_t packed[2] = {0u, 0u};
@@ -170,7 +172,9 @@ __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, 
   } else {
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-      const uint32_t mag = (s != 0u) ? e2m1_rne(fminf(fabsf(v[i]) / sg, 6.0f)) : 0u;
+      // a zero element gets code 0 even where s g has underflowed to 0 (0 / 0 counts as 0);
+      // a non-zero one over s g = 0 saturates at 6
+      const uint32_t mag = (s != 0u && fabsf(v[i]) > 0.f) ? e2m1_rne(fminf(fabsf(v[i]) / sg, 6.0f)) : 0u;
       packed[i >> 3] |= mag << (4 * (i & 7));
     }
   }

@@ -83,6 +83,14 @@ int moe_last_hip_error(void);
 /* ---------------------------------------------------------------------------
  * 1. Routing and permutation.
  *
+ * Defined by: the layer the pages measure routes every token to 8 of 256 experts, so
+ * that at 1024 concurrent requests each expert sees about 32 rows ("Tracing the
+ * Failure: Debugging CUTLASS FP4 Tile Configurations on Blackwell SM120", section "The
+ * Broader Context"; "Peering into the Kernel", section "Input Knowledge Required"); the
+ * grouped GEMM then runs one small GEMM per expert over a per-expert size array (same
+ * first page, section "Input Knowledge Required").  The pages fix neither the router
+ * arithmetic nor the row order, so this call takes the plainest readings: softmax over
+ * the chosen logits, ties to the lower id, rows of a group in token order.
  * logits [T, E] f32 row-major.  For each token the k largest logits are taken in
  * descending order, equal logits going to the lower expert id:
  *   topk_ids [T, k] i32, topk_w [T, k] f32 = softmax over the k chosen logits
@@ -105,6 +113,12 @@ moe_status moe_route_permute(const float *logits, int T, int E, int k, int32_t *
 /* ---------------------------------------------------------------------------
  * 2. NVFP4 quantisation of x [rows, C] (C % 16 == 0), blocks of 16 along C.
  *
+ * Defined by: the operand format the pages budget shared memory for -- packed 4-bit
+ * elements and one 8-bit FP8 scale per 16 elements along K, for both operands
+ * ("Cracking the SM120 Shared Memory Ceiling", sections "The Shared Memory
+ * Calculation" and "Input Knowledge Required").  The pages give no quantisation
+ * recipe; the global scale, the rounding of the block scale and of the elements below
+ * are this library's readings (round to nearest even, saturating).
  * x_dtype: MOE_DTYPE_BF16 (x is uint16 bf16 bit patterns) or MOE_DTYPE_F32.
  * gs_mode MOE_GS_DYNAMIC: g = amax / 2688 in binary32 (1 if amax is 0), written
  *   to *gs; amax is max|x| over the whole tensor, or, when amax_in is not NULL,
@@ -113,7 +127,9 @@ moe_status moe_route_permute(const float *logits, int T, int E, int k, int32_t *
  * gs_mode MOE_GS_STATIC: g is read from *gs.
  * Then per block b: t = amax_b / (6 g), s = e4m3(min(t, 448)) (round to nearest
  * even), and per element u = |x| / (s g), code = sign(x) | e2m1(min(u, 6))
- * (round to nearest even); a block with s = 0 holds signed zeros.  Every step
+ * (round to nearest even); a block with s = 0 holds signed zeros.  Zero stays zero
+ * where g or s g has underflowed to 0: 0 / 0 counts as 0 (a zero block gets s = 0, a zero
+ * element magnitude code 0), a non-zero element over s g = 0 saturates at 6.  Every step
  * is a correctly rounded binary32 operation, so the output is bit-exact.
  * q [rows, C/2] u8, sf [rows, C/16] u8, gs: one f32.
  * Limits: rows >= 0, C >= 16, rows*C < 2^40.  ws: moe_quantize_nvfp4_workspace().
@@ -128,6 +144,16 @@ moe_status moe_quantize_nvfp4(const void *x, int x_dtype, int64_t rows, int64_t 
 /* ---------------------------------------------------------------------------
  * 3. Grouped NVFP4 GEMM.
  *
+ * Defined by: FP4 x FP4 -> BF16 block-scaled GEMMs, one per expert, in one grouped
+ * launch over a per-expert problem-size array ("Tracing the Failure: Debugging CUTLASS
+ * FP4 Tile Configurations on Blackwell SM120", sections "The Broader Context" and "Input
+ * Knowledge Required"; the kernel instantiation in "The CUTLASS Tile That Wouldn't Fit:
+ * Debugging EP8 on Blackwell SM120", section "The Crash: A Deep-Dive into CUTLASS Tile
+ * Geometry"), with the NONE pass-through epilogue ("The Epilogue That Broke the Kernel",
+ * section "The Insight: FINALIZE vs NONE").  SwiGLU between the two projections is this
+ * library's reading of the expert MLP (gate columns first).  The can-implement check is
+ * exact, unlike the one traced in "Cracking the SM120 Shared Memory Ceiling", section
+ * "Tracing the Failure", which passed a configuration that then failed to initialise.
  * For expert e and permuted row p in [expert_offsets[e], expert_offsets[e+1]):
  *   y[p, n] = gA * gB[e] * sum_kb sA[r, kb] sB[e, n, kb] sum_{i<16} a[r, 16kb+i] b[e, n, 16kb+i]
  * with r = A_rows ? A_rows[p] : p.  Products are exact (fp16 MFMA on operands
@@ -199,7 +225,9 @@ moe_status moe_grouped_gemm_nvfp4(const moe_gemm_args *args, void *ws, size_t ws
                                   hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
- * 3b. One-time weight preparation: regroup NVFP4 weights [rows, K] (codes B [rows, K/2],
+ * 3b. One-time weight preparation (this library's own layout; the pages load their tiles
+ * with TMA instead, "Peering into the Kernel", section "Input Knowledge Required"):
+ * regroup NVFP4 weights [rows, K] (codes B [rows, K/2],
  * scales B_sf [rows, K/16]; rows = E*N) into the packed layout the grouped GEMM streams:
  * per 16-row tile T and 256-wide K step s, a 2304-byte block at offset (T*K/256 + s)*2304
  * holding, in the order the 64 lanes of a wave load them (lane 16g + r, row 16T + r), two
@@ -213,7 +241,12 @@ moe_status moe_pack_weights_nvfp4(const uint8_t *B, const uint8_t *B_sf, int64_t
                                   uint8_t *packed, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
- * 4. FINALIZE: out[t, h] = bf16(sum_{j<k} topk_w[t, j] * Y[token_slot_row[t*k+j], h]),
+ * 4. FINALIZE.  Defined by: the FINALIZE epilogue mode the pages contrast with NONE
+ * ("The Epilogue That Broke the Kernel", section "The Insight: FINALIZE vs NONE"), whose
+ * staging they price as an FP32 accumulator with a BF16 output ("Cracking the SM120
+ * Shared Memory Ceiling", section "The Shared Memory Calculation"); its arithmetic is
+ * read as the router-weighted sum of each token's k expert rows into BF16.
+ * out[t, h] = bf16(sum_{j<k} topk_w[t, j] * Y[token_slot_row[t*k+j], h]),
  * summed in binary32 in slot order (a per-token gather-reduce: no atomics,
  * deterministic).  Y bf16 [R, H], topk_w f32 [T, k], token_slot_row i32 [T*k],
  * out bf16 [T, H].  Limits: T >= 0, 1 <= k <= 32, H % 8 == 0, H >= 8.

@@ -44,7 +44,6 @@ def lib():
             "orc_bf16_round": (C.c_uint16, [f64]),
             "orc_bf16_value": (f64, [C.c_uint16]),
             "orc_quantize_nvfp4": (None, [P, i64, i64, i32, f32, P, P, P]),
-            "orc_nvfp4_value": (f64, [P, P, f32, i64, i64, i64]),
             "orc_route": (None, [P, i32, i32, i32, P, P]),
             "orc_permute": (None, [P, i32, i32, i32, P, P, P]),
             "orc_grouped_gemm_rows": (None, [P, P, f32, P, P, P, P, P, i32, i32, i32, P, i64, P]),
@@ -106,16 +105,6 @@ class NVFP4:
     @property
     def shape(self):
         return (self.q.shape[0], self.q.shape[1] * 2)
-
-    def dequant(self) -> np.ndarray:
-        """FP64 values, elementwise through the oracle's decode."""
-        rows, cols = self.shape
-        L = lib()
-        out = np.empty((rows, cols), np.float64)
-        for r in range(rows):
-            for c in range(cols):
-                out[r, c] = L.orc_nvfp4_value(_p(self.q), _p(self.sf), self.g, cols, r, c)
-        return out
 
 
 def quantize(x: np.ndarray, g: float | None = None) -> NVFP4:

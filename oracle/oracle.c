@@ -118,7 +118,9 @@ void orc_quantize_nvfp4(const float *x, int64_t rows, int64_t C, int dynamic,
         float a = fabsf(xb[i]);
         if (a > amax_b) amax_b = a;
       }
-      float t = amax_b / six_g;
+      /* a zero block has scale 0 even when 6 g is 0 (an underflowed g): 0 / 0
+       * counts as 0, not NaN */
+      float t = (amax_b > 0.0f) ? amax_b / six_g : 0.0f;
       if (t > 448.0f) t = 448.0f;
       int s = orc_e4m3_round(t);
       sf[r * nblk + b] = (uint8_t)s;
@@ -130,7 +132,9 @@ void orc_quantize_nvfp4(const float *x, int64_t rows, int64_t C, int dynamic,
           float v = xb[i + h];
           int sign = signbit(v) ? 8 : 0;
           int mag = 0;
-          if (s_val != 0.0f) {
+          /* a zero element has code 0 even when s * g underflows to 0 (0 / 0
+           * counts as 0); a non-zero element over a zero s * g saturates at 6 */
+          if (s_val != 0.0f && fabsf(v) > 0.0f) {
             float u = fabsf(v) / sg;
             if (u > 6.0f) u = 6.0f;
             mag = orc_e2m1_round(u);
@@ -141,13 +145,6 @@ void orc_quantize_nvfp4(const float *x, int64_t rows, int64_t C, int dynamic,
       }
     }
   }
-}
-
-double orc_nvfp4_value(const uint8_t *q, const uint8_t *sf, float g, int64_t C,
-                       int64_t r, int64_t c) {
-  uint8_t byte = q[r * (C / 2) + c / 2];
-  int code = (c & 1) ? (byte >> 4) : (byte & 15);
-  return orc_e2m1_value(code) * orc_e4m3_value(sf[r * (C / 16) + c / 16]) * (double)g;
 }
 
 /* ---- routing ---- */

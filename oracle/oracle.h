@@ -58,14 +58,13 @@ double orc_bf16_value(uint16_t b);
  * dynamic == 0: g = g_in.
  * Per block: t = amax_b / (6 g); s = e4m3(min(t, 448)); u = |x| / (s g);
  * code = sign(x) | e2m1(min(u, 6)); blocks with s == 0 hold signed zeros.
+ * Zero stays zero where g or s * g has underflowed to 0: a block whose maximum
+ * is 0 gets s = 0 and a zero element gets magnitude code 0 (0 / 0 counts as 0);
+ * a non-zero element over s * g == 0 saturates at 6.
  * q[rows, C/2]: element 2i in the low nibble of byte i.  sf[rows, C/16].
  */
 void orc_quantize_nvfp4(const float *x, int64_t rows, int64_t C, int dynamic,
                         float g_in, uint8_t *q, uint8_t *sf, float *g_out);
-
-/* Dequantised value of element (r, c) of an NVFP4 tensor with C columns. */
-double orc_nvfp4_value(const uint8_t *q, const uint8_t *sf, float g, int64_t C,
-                       int64_t r, int64_t c);
 
 /*
  * Top-k routing of logits[T, E]: the k largest logits of each token in

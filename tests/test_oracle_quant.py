@@ -116,3 +116,45 @@ def test_saturation_at_448():
     t = oracle.quantize(x, g=1e-3)
     assert t.sf[0, 1] == 0x7E           # amax_b / (6 g) far above 448 -> 448
     assert codes_of(t.q)[0, 16] == 7    # |x| / (448 g) far above 6 -> 6
+
+
+def test_underflowed_global_scale_keeps_zeros():
+    """An all-subnormal tensor whose global scale amax / 2688 underflows to 0 in binary32
+    (numpy's own float32 division says so): 6 g = 0, so a block with a non-zero maximum gets
+    t = +inf -> scale 448 (0x7E) and its non-zero elements saturate at 6 (code 7 with their
+    sign), while zero stays zero -- a zero block keeps scale 0 and a zero element code 0
+    (0 / 0 counts as 0 in the reading)."""
+    tiny = np.float32(2.0 ** -149)
+    x = np.zeros((2, 48), np.float32)
+    x[0, :16] = tiny * np.arange(-8, 8, dtype=np.float32)     # zeros among small values
+    x[1, 32:48] = -tiny * 40
+    x[1, 33] = -0.0
+    amax = np.abs(x).max()
+    assert np.float32(amax) / np.float32(2688.0) == 0.0
+    t = oracle.quantize(x)
+    assert t.g == 0.0
+    c = codes_of(t.q)
+    assert t.sf[0, 0] == 0x7E and t.sf[1, 2] == 0x7E
+    assert np.all(t.sf[0, 1:] == 0) and np.all(t.sf[1, :2] == 0)
+    row0 = x[0, :16]
+    want = np.where(row0 == 0, 0, 7) | np.where(np.signbit(row0), 8, 0)
+    assert np.array_equal(c[0, :16], want)
+    assert np.all(c[0, 16:] == 0) and np.all(c[1, :32] == 0)
+    assert c[1, 33] == 8 and np.all(np.delete(c[1, 32:48], 1) == 15)
+
+
+def test_underflowed_block_divisor_keeps_zeros():
+    """Static g = 2^-149: a block with maximum 3 * 2^-149 gets t = 0.5 exactly, scale 0.5
+    (0x30), and s g = 2^-150 rounds to 0 in binary32 (numpy).  Its zero elements keep code 0
+    (0 / 0 counts as 0), its non-zero ones saturate at 6; a block of ordinary values under the
+    same g saturates its scale at 448 and is quantised normally."""
+    g = np.float32(2.0 ** -149)
+    assert np.float32(0.5) * g == 0.0
+    x = np.zeros((1, 32), np.float32)
+    x[0, :4] = np.array([3, 0, -1, -0.0], np.float32) * g
+    x[0, 16:32] = np.float32(1.0)
+    t = oracle.quantize(x, g=float(g))
+    c = codes_of(t.q)
+    assert t.sf[0, 0] == 0x30 and t.sf[0, 1] == 0x7E
+    assert list(c[0, :4]) == [7, 0, 15, 8] and np.all(c[0, 4:16] == 0)
+    assert np.all(c[0, 16:32] == 7)   # 1 / (448 g) is far above 6
