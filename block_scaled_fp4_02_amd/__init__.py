@@ -33,7 +33,7 @@ EXPORTED = [
     "moe_route_permute_workspace", "moe_route_permute",
     "moe_quantize_nvfp4_workspace", "moe_quantize_nvfp4",
     "moe_grouped_gemm_nvfp4_workspace", "moe_grouped_gemm_nvfp4_amax_slots",
-    "moe_grouped_gemm_nvfp4_can_implement", "moe_grouped_gemm_nvfp4",
+    "moe_grouped_gemm_nvfp4_can_implement", "moe_grouped_gemm_nvfp4", "moe_grouped_gemm_nvfp4_noalloc",
     "moe_pack_weights_nvfp4_bytes", "moe_pack_weights_nvfp4",
     "moe_finalize",
 ]
@@ -84,6 +84,7 @@ def lib():
             "moe_grouped_gemm_nvfp4_amax_slots": (i64, [args_p]),
             "moe_grouped_gemm_nvfp4_can_implement": (i32, [args_p]),
             "moe_grouped_gemm_nvfp4": (i32, [args_p, P, sz, P]),
+            "moe_grouped_gemm_nvfp4_noalloc": (i32, [args_p, P]),
             "moe_pack_weights_nvfp4_bytes": (sz, [i64, i32]),
             "moe_pack_weights_nvfp4": (i32, [P, P, i64, i32, P, P]),
             "moe_finalize": (i32, [P, i64, P, P, i32, i32, i32, P, P]),
@@ -173,6 +174,16 @@ def moe_grouped_gemm_nvfp4_can_implement(args: moe_gemm_args) -> int:
 def moe_grouped_gemm_nvfp4(args: moe_gemm_args, ws, stream=None):
     _check("moe_grouped_gemm_nvfp4",
            lib().moe_grouped_gemm_nvfp4(C.byref(args), _p(ws), ws.numel(), _stream(stream)))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def moe_grouped_gemm_nvfp4_noalloc(args: moe_gemm_args, stream=None):
+    """The grouped GEMM with the library's static device scratch in place of a workspace
+    (nothing is allocated; calls that overlap on one GPU race)."""
+    _check("moe_grouped_gemm_nvfp4_noalloc",
+           lib().moe_grouped_gemm_nvfp4_noalloc(C.byref(args), _stream(stream)))
 
 
 def moe_pack_weights_nvfp4(B, B_sf, packed, stream=None):

@@ -3,9 +3,42 @@
 // caller's stream.  No entry point allocates, synchronises or throws.
 #include "common.hpp"
 
+#include <mutex>
+
 namespace moe {
 namespace {
 thread_local int g_last_hip_error = 0;
+
+// ---- scratch of the no-allocation grouped GEMM -------------------------------------------
+//
+// A static device array holds the grouped GEMM's workspace (the work-item list and its count)
+// for moe_grouped_gemm_nvfp4_noalloc.  Every GPU the library runs on holds its own copy at
+// its own address until the process ends.  On the host `scratch` is only a stand-in for the
+// device variable: its device address is looked up once per device, with that device
+// current, and only that address is ever passed to a kernel.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+static_assert(kNoAllocScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "scratch size differs from the header");
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, null until looked up
+
+hipError_t device_scratch(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 }  // namespace
 
 moe_status launch_status(hipError_t e) {
@@ -127,6 +160,17 @@ moe_status moe_grouped_gemm_nvfp4(const moe_gemm_args *args, void *ws, size_t ws
   if (st != MOE_OK) return st;
   const GemmPlan plan = plan_gemm(*args);
   if (!ws || ws_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE;
+  return launch_status(launch_grouped_gemm(*args, plan, ws, stream));
+}
+
+moe_status moe_grouped_gemm_nvfp4_noalloc(const moe_gemm_args *args, hipStream_t stream) {
+  const moe_status st = check_gemm(args, true);
+  if (st != MOE_OK) return st;
+  const GemmPlan plan = plan_gemm(*args);
+  if (plan.ws_bytes > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+  void *ws = nullptr;
+  const hipError_t e = device_scratch(&ws);
+  if (e != hipSuccess) return launch_status(e);
   return launch_status(launch_grouped_gemm(*args, plan, ws, stream));
 }
 

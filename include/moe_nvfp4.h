@@ -38,7 +38,8 @@
  *  - Every data pointer is a DEVICE pointer on the current HIP device, owned by
  *    the caller; the library allocates no device memory, keeps no pointer after
  *    it returns and holds no global state apart from a thread-local last HIP
- *    error code.  Tensor base pointers are 16-byte aligned (as every device
+ *    error code and the static scratch array of moe_grouped_gemm_nvfp4_noalloc
+ *    (section 3a).  Tensor base pointers are 16-byte aligned (as every device
  *    allocation is) and tensors are dense, row-major.
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream); no call
  *    synchronises with the device or copies device data to the host.
@@ -223,6 +224,22 @@ int64_t moe_grouped_gemm_nvfp4_amax_slots(const moe_gemm_args *args);
 moe_status moe_grouped_gemm_nvfp4_can_implement(const moe_gemm_args *args);
 moe_status moe_grouped_gemm_nvfp4(const moe_gemm_args *args, void *ws, size_t ws_bytes,
                                   hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * 3a. The grouped GEMM without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops or harnesses that forbid
+ * allocation).  Same arguments, validation, results and kernels as
+ * moe_grouped_gemm_nvfp4; the workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (1 MiB) inside the library instead, one per GPU, held until
+ * the process ends.  Returns MOE_ERR_WORKSPACE when the launch needs more than that
+ * (moe_grouped_gemm_nvfp4_workspace() > MOE_NOALLOC_SCRATCH_BYTES, about 65,000 work
+ * items); calls nothing that allocates.  The first call on a device looks up that
+ * device's copy of the array (a failure there returns MOE_ERR_HIP).  Every call on a GPU
+ * shares that GPU's array: calls that may overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.
+ * ------------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES (1u << 20)
+moe_status moe_grouped_gemm_nvfp4_noalloc(const moe_gemm_args *args, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * 3b. One-time weight preparation (this library's own layout; the pages load their tiles

@@ -256,3 +256,20 @@ def test_host_queries_survive_random_and_hostile_arguments():
         L.moe_quantize_nvfp4_workspace(rows, cols)
         T, E, k = int(rng.integers(-5, 1 << 20)), int(rng.integers(-5, 2000)), int(rng.integers(-5, 40))
         L.moe_route_permute_workspace(T, E, k)
+
+
+def test_noalloc_gemm_refuses_launches_beyond_its_scratch():
+    """The no-allocation grouped GEMM validates like the workspace entry point and refuses, on
+    the host and before any HIP call, a launch whose work list exceeds its static scratch."""
+    L = moe.lib()
+    # 65536 experts of one row each: ~65,536 x 24 items of 16 bytes, far beyond 1 MiB
+    a = moe.moe_gemm_args()
+    a.A, a.A_sf, a.A_gs, a.B, a.B_gs, a.expert_offsets, a.D = (FAKE,) * 7
+    a.rows_A, a.E, a.N, a.K, a.R = 65536, 65536, 6144, 256, 65536
+    a.epilogue, a.B_layout = moe.MOE_EPI_NONE, moe.MOE_LAYOUT_PACKED
+    assert L.moe_grouped_gemm_nvfp4_can_implement(C.byref(a)) == moe.MOE_OK
+    assert L.moe_grouped_gemm_nvfp4_workspace(C.byref(a)) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert L.moe_grouped_gemm_nvfp4_noalloc(C.byref(a), None) == moe.MOE_ERR_WORKSPACE
+    a.E = 0
+    assert L.moe_grouped_gemm_nvfp4_noalloc(C.byref(a), None) == moe.MOE_ERR_SHAPE
+    assert L.moe_grouped_gemm_nvfp4_noalloc(None, None) == moe.MOE_ERR_NULL
