@@ -86,26 +86,70 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
-def copy_bandwidth(torch, mib: int = 2048, launches: int = 10) -> float:
-    """Bytes moved per second (read + write) by a plain device-to-device copy of `mib` MiB:
-    the streaming rate the machine's HBM reaches on this image, a measured companion to the
-    8 TB/s spec peak."""
-    n = mib << 20
-    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
-    for _ in range(2):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(launches):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    gbps = 2.0 * n * launches / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+_probe = None
+
+
+def stream_probe():
+    """The streaming-read measurement kernel (block_scaled_fp4_02_amd/libmoe_stream_probe.so)."""
+    global _probe
+    if _probe is None:
+        import ctypes as C
+        path = os.path.join(ROOT, "block_scaled_fp4_02_amd", "libmoe_stream_probe.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+        L = C.CDLL(path)
+        L.moe_probe_stream_read_variants.restype = C.c_int
+        L.moe_probe_stream_read_variant_info.restype = C.c_int
+        L.moe_probe_stream_read_variant_info.argtypes = [C.c_int]
+        L.moe_probe_stream_read_groups.restype = C.c_int64
+        L.moe_probe_stream_read_groups.argtypes = [C.c_int64, C.c_int, C.c_int64]
+        L.moe_probe_stream_read.restype = C.c_int
+        L.moe_probe_stream_read.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_int64, C.c_void_p, C.c_void_p]
+        _probe = L
+    return _probe
+
+
+def stream_read(torch, nbytes: int, copies: int, launches: int) -> dict:
+    """The streaming-read kernel over one of `copies` distinct buffers of `nbytes` each, cycled
+    (together larger than the 256 MB of on-die cache when copies > 1, so every launch reads
+    HBM), HIP events on the launch stream.  Every variant (loads in flight per lane, cache
+    policy) and grid (one round over the buffer, or 2, 4 or 8 looping workgroups per CU) is
+    timed; the fastest is the measured read rate at this size."""
+    import ctypes as C
+    L = stream_probe()
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(copies)]
+    sink = torch.empty(4 * (1 << 19), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = C.c_void_p(stream.cuda_stream)
+    best = None
+    for v in range(L.moe_probe_stream_read_variants()):
+        for max_groups in (1 << 19, 256 * 8, 256 * 4, 256 * 2):
+            groups = int(L.moe_probe_stream_read_groups(nbytes, v, max_groups))
+
+            def launch(i):
+                rc = L.moe_probe_stream_read(C.c_void_p(bufs[i % copies].data_ptr()), nbytes, v, groups,
+                                             C.c_void_p(sink.data_ptr()), sp)
+                if rc != 0:
+                    raise RuntimeError(f"moe_probe_stream_read: hipError {rc}")
+            for i in range(2 * copies):
+                launch(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(launches):
+                launch(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / launches
+            if best is None or us < best[0]:
+                info = L.moe_probe_stream_read_variant_info(v)
+                best = (us, {"loads_in_flight_per_lane": info & 255, "non_temporal": bool(info & 256),
+                             "workgroups": groups})
+    del bufs, sink
     torch.cuda.empty_cache()
-    return gbps
+    us, how = best
+    return {"bytes_per_launch": nbytes, "copies_rotated": copies, "avg_launch_us": round(us, 2),
+            "GBps": round(nbytes / us / 1e3, 1), "best_variant": how}
 
 
 def power_sample(moe, torch):
@@ -171,7 +215,7 @@ def make_weights(L, moe, torch):
     return out["W1"], out["W2"]
 
 
-def grouped_gemm_decode(moe, torch, steps: int, copies: int = 8) -> dict:
+def grouped_gemm_decode(moe, torch, steps: int, copies: int = 8, with_stream_read: bool = True) -> dict:
     """The single grouped GEMM at decode shape (8 groups x 32 rows, K 6144, N 2048, NONE
     epilogue) on packed weights.  `copies` distinct weight copies (8 x 56.6 MB, more than
     the 256 MB Infinity Cache) are cycled so that every launch streams its weights from HBM."""
@@ -207,9 +251,18 @@ def grouped_gemm_decode(moe, torch, steps: int, copies: int = 8) -> dict:
     w_bytes = G.E * G.N * (G.K // 2 + G.K // 16)
     alg = w_bytes + R * (G.K // 2 + G.K // 16) + R * G.N * 2
     flops = 2.0 * R * G.N * G.K
-    return {"workload": G.name, "avg_launch_us": round(us, 2), "tflops": round(flops / us / 1e6, 2),
+    del Ws, args, packed, A, D, ws
+    torch.cuda.empty_cache()
+    # the streaming-read kernel over exactly as many bytes per launch, cycled over as many
+    # copies: the read rate this working-set size reaches, launch start and drain included
+    rec = {"workload": G.name, "avg_launch_us": round(us, 2), "tflops": round(flops / us / 1e6, 2),
             "alg_bytes_per_launch": alg, "GBps": round(alg / us / 1e3, 1),
             "hbm_frac": round(alg / us / 1e3 / HBM_PEAK_GBPS, 4), "weight_copies_rotated": copies}
+    if with_stream_read:
+        sr = stream_read(torch, (alg + 15) // 16 * 16, copies, n)
+        rec["stream_read_same_bytes"] = sr
+        rec["frac_of_stream_read_same_bytes"] = round(sr["avg_launch_us"] / us, 4)
+    return rec
 
 
 def dense_gemm(moe, torch, launches: int = 20) -> dict:
@@ -423,6 +476,7 @@ def roofline_record(L, r) -> dict:
                 "achieved": round(tf, 1), "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tf / F16_PEAK_TFLOPS, 4), "traffic": None,
                 "flops_per_launch": int(r["g1_flops"]), "avg_launch_us": round(g1_s * 1e6, 2),
+                "peak_dtype": "f16 (the exact E2M1 x E4M3 products are formed in fp16)",
                 "frac_of_fp4_dense_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
     return {"kernel": "gemm_lds_kernel<1> (gate/up + SwiGLU)", "bound": "hbm",
             "achieved": round(r["g1_alg_bytes"] / g1_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -441,6 +495,29 @@ def shard_record(L, moe, torch, steps: int, weights=None) -> dict:
            "weight_hbm_frac": round(r["weight_gbps"] / HBM_PEAK_GBPS, 4),
            "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
            "offsets": [int(v) for v in r["off"]]}
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
+def prefill_record(L, moe, torch, steps: int, weights) -> dict:
+    """The prefill layer on the full path, with the roofline of its two GEMMs against the
+    fp16 dense MFMA peak (and the FP4 peak beside it)."""
+    r = run_layer(L, moe, torch, steps, 2, weights=weights)
+    g1_s, g2_s = r["stage_us"]["gemm1"] * 1e-6, r["stage_us"]["gemm2"] * 1e-6
+    g2_flops = 2.0 * int(r["off"][-1]) * L.H * L.I
+    tf1, tf2 = r["g1_flops"] / g1_s / 1e12, g2_flops / g2_s / 1e12
+    sizes = r["sizes"]
+    out = {"workload": L.name, "steps": steps, "ms_per_step": round(r["ms_per_step"], 4),
+           "tflops": round(r["value"], 2), "gemm_tflops": round(r["gemm_tflops"], 2),
+           "rows_per_expert_min_median_max": [int(sizes.min()), int(np.median(sizes)), int(sizes.max())],
+           "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
+           "roofline": roofline_record(L, r),
+           "gemm2": {"kernel": "gemm_lds_wide_kernel<0> (down, NONE)", "achieved": round(tf2, 1),
+                     "unit": "TFLOP/s", "frac": round(tf2 / F16_PEAK_TFLOPS, 4),
+                     "frac_of_fp4_dense_peak": round(tf2 / FP4_PEAK_TFLOPS, 4)},
+           "gemms_frac_of_f16_dense_peak": round(r["gemm_tflops"] / F16_PEAK_TFLOPS, 4),
+           "gemms_frac_of_fp4_dense_peak": round(r["gemm_tflops"] / FP4_PEAK_TFLOPS, 4)}
     del r
     torch.cuda.empty_cache()
     return out
@@ -510,12 +587,16 @@ def main():
         sk["rows_per_expert_min_median_max"] = [int(sizes_sk.min()), int(np.median(sizes_sk)), int(sizes_sk.max())]
         sk["active_experts"] = int((sizes_sk > 0).sum())
         rec["layer_skewed"] = sk
+        # prefill (16384 tokens, ~512 rows per expert): the MFMA-bound configuration, on the
+        # same expert weights (same expert count, hidden and intermediate sizes)
+        rec["layer_prefill"] = prefill_record(synth.LAYER_PREFILL, moe, torch, min(args.steps, 10), r["weights"])
     del r
     torch.cuda.empty_cache()
     if rec["roofline"]["bound"] == "hbm":
-        copy_gbps = copy_bandwidth(torch)
-        rec["roofline"]["measured_copy_GBps"] = round(copy_gbps, 1)
-        rec["roofline"]["frac_of_measured_copy"] = round(rec["roofline"]["achieved"] / copy_gbps, 4)
+        # measured companion to the spec peak: the streaming-read kernel over 1 GiB buffers
+        sr = stream_read(torch, 1 << 30, 2, 20)
+        rec["roofline"]["measured_stream_read_GBps"] = sr["GBps"]
+        rec["roofline"]["frac_of_measured_stream_read"] = round(rec["roofline"]["achieved"] / sr["GBps"], 4)
     else:
         mm = torch_f16_matmul_tflops(torch)
         rec["roofline"]["measured_f16_matmul_TFLOPs"] = round(mm, 1)

@@ -18,6 +18,9 @@ BUILD_DIR = os.path.join(ROOT, "_build", "moe_nvfp4")
 LIB_PATH = os.path.join(PKG, "libmoe_nvfp4.so")
 SOURCES = ["route_permute.hip", "quantize.hip", "grouped_gemm.hip", "gemm_lds.hip", "gemm_ksplit.hip",
            "gemm_rowmajor.hip", "finalize.hip", "moe_api.hip"]
+# the benchmark's streaming-read measurement kernel, a library of its own (not the MoE ABI)
+PROBE_SOURCES = ["stream_probe.hip"]
+PROBE_LIB_PATH = os.path.join(PKG, "libmoe_stream_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH_FLAGS = ["--offload-arch=gfx950"]
@@ -40,18 +43,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [HIPCC, *ARCH_FLAGS, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    allsrc = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(min(len(allsrc), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, allsrc))
+    _link(objs[:len(SOURCES)], LIB_PATH)
+    _link(objs[len(SOURCES):], PROBE_LIB_PATH)
     if verbose:
-        print("built", LIB_PATH)
+        print("built", LIB_PATH, "and", PROBE_LIB_PATH)
     return LIB_PATH
 
 
