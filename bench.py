@@ -28,7 +28,8 @@ HBM_PEAK_GBPS = 8000.0
 F16_PEAK_TFLOPS = 2500.0   # dense fp16 MFMA: the ceiling of the exact NVFP4 path
 FP4_PEAK_TFLOPS = 10100.0  # dense FP4 MFMA (power-of-two scales per 32 only): context
 WORKLOADS = {"layer_decode": "LAYER_DECODE", "layer_skewed": "LAYER_SKEWED", "layer_prefill": "LAYER_PREFILL",
-             "layer_tiny": "TINY", "layer_ep8": "LAYER_EP8", "layer_tp8": "LAYER_TP8"}
+             "layer_tiny": "TINY", "layer_ep8": "LAYER_EP8", "layer_tp8": "LAYER_TP8",
+             "gemm_e8_m32": "GEMM_DECODE"}
 
 
 def parse():
@@ -39,6 +40,9 @@ def parse():
     ap.add_argument("--workload", default="layer_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the named workload (no further configurations or measured peaks); "
+                         "for short profiler runs")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times (to scale HBM "
                          "byte counters against a kernel of known traffic) and exit")
@@ -545,6 +549,10 @@ def main():
     import synth
     L = getattr(synth, WORKLOADS[args.workload])
     torch.cuda.set_device(0)
+    if args.workload == "gemm_e8_m32":
+        # the single grouped GEMM alone (8 groups x 32 rows, K 6144, N 2048, NONE epilogue)
+        print(json.dumps(grouped_gemm_decode(moe, torch, args.steps, with_stream_read=not args.no_extras)), flush=True)
+        return
     r = run_layer(L, moe, torch, args.steps, args.warmup)
     sizes, g1_s = r["sizes"], r["g1_s"]
     rec = {
@@ -572,7 +580,8 @@ def main():
         "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
     }
     off, row_src = r["off"], r["plan"].row_src.cpu().numpy()
-    if L is synth.LAYER_DECODE:
+    extras = not args.no_extras
+    if L is synth.LAYER_DECODE and extras:
         f = run_layer(L, moe, torch, args.steps, args.warmup, weights=r["weights"], fused=True)
         rec["layer_decode_fused_static_g2"] = {
             "ms_per_step": round(f["ms_per_step"], 4), "tflops": round(f["value"], 2),
@@ -592,16 +601,16 @@ def main():
         rec["layer_prefill"] = prefill_record(synth.LAYER_PREFILL, moe, torch, min(args.steps, 10), r["weights"])
     del r
     torch.cuda.empty_cache()
-    if rec["roofline"]["bound"] == "hbm":
+    if extras and rec["roofline"]["bound"] == "hbm":
         # measured companion to the spec peak: the streaming-read kernel over 1 GiB buffers
         sr = stream_read(torch, 1 << 30, 2, 20)
         rec["roofline"]["measured_stream_read_GBps"] = sr["GBps"]
         rec["roofline"]["frac_of_measured_stream_read"] = round(rec["roofline"]["achieved"] / sr["GBps"], 4)
-    else:
+    elif extras:
         mm = torch_f16_matmul_tflops(torch)
         rec["roofline"]["measured_f16_matmul_TFLOPs"] = round(mm, 1)
         rec["roofline"]["frac_of_measured_f16_matmul"] = round(rec["roofline"]["achieved"] / mm, 4)
-    if L is synth.LAYER_DECODE:
+    if L is synth.LAYER_DECODE and extras:
         rec["grouped_gemm_decode_8x32"] = grouped_gemm_decode(moe, torch, args.steps)
         rec["dense_gemm_8192"] = dense_gemm(moe, torch)
         for key, Ls in (("shard_ep8", synth.LAYER_EP8), ("shard_tp8", synth.LAYER_TP8)):
