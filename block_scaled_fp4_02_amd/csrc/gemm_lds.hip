@@ -374,21 +374,38 @@ __device__ __forceinline__ void lds_k1_body(const Params &P, LdsShared<kChunkTil
         }
       }
     }
-    // 16x16 D lane layout: weight row 4g + i of tile j, token row r of tile mt
+    // 16x16 D lane layout: weight row 4g + i of tile j, token row r of tile mt.  A lane holds
+    // 4 consecutive columns of one row, so storing from registers writes 16 separate 32-byte
+    // pieces per instruction.  Instead each wave stages its 64 bf16 columns of every row in
+    // the second activation buffer (unused with one K step): 128 B per row, its eight 16-byte
+    // pieces XOR-swizzled by the row so that the 8-byte writes of the MFMA layout spread over
+    // the banks; then each lane stores one 16-byte piece and 8 lanes write a whole 128-byte
+    // row piece.  The area is private to the wave: 4 waves x 48 rows x 128 B = the buffer.
+    uint4 *stage = &sh.a[1][0][0][0] + wv * (kChunkTiles * 16 * 8);
 #pragma unroll
     for (int mt = 0; mt < NM; mt++) {
       const int m = mt * 16 + r;
-      if (m < nrows) {
-        uint16_t *drow = static_cast<uint16_t *>(P.D) + (row0 + m) * static_cast<int64_t>(P.N);
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const uint32_t lo = f32_to_bf16(acc[j][mt][0] * gscale) |
-                              (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][1] * gscale)) << 16);
-          const uint32_t hi = f32_to_bf16(acc[j][mt][2] * gscale) |
-                              (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][3] * gscale)) << 16);
-          *reinterpret_cast<uint2 *>(drow + col0 + t * 256 + j * 16 + 4 * g) = make_uint2(lo, hi);
-        }
+      for (int j = 0; j < 4; j++) {
+        const uint32_t lo = f32_to_bf16(acc[j][mt][0] * gscale) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][1] * gscale)) << 16);
+        const uint32_t hi = f32_to_bf16(acc[j][mt][2] * gscale) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[j][mt][3] * gscale)) << 16);
+        const int piece = (2 * j + (g >> 1)) ^ (m & 7);   // columns 16j + 4g .. + 3
+        reinterpret_cast<uint2 *>(stage + m * 8 + piece)[g & 1] = make_uint2(lo, hi);
       }
+    }
+    __syncthreads();
+    // lane: row 8k + (lane >> 3) of round k, piece c = lane & 7; the row's swizzle
+    // (lane >> 3) ^ c is the same in every round
+    const int rl = lane >> 3, c = lane & 7;
+    const uint4 *src = stage + rl * 8 + (c ^ rl);
+    uint16_t *dst = static_cast<uint16_t *>(P.D) + (row0 + rl) * static_cast<int64_t>(P.N) + col0 + t * 256 + 8 * c;
+    const int64_t dst_step = 8 * static_cast<int64_t>(P.N);
+#pragma unroll
+    for (int k = 0; k < 2 * NM; k++) {
+      const uint4 v = src[64 * k];
+      if (8 * k + rl < nrows) *reinterpret_cast<uint4 *>(dst + k * dst_step) = v;
     }
   };
 #pragma unroll 1
