@@ -48,6 +48,10 @@ struct Params {
 // (one wave-wide pass, an expert per lane); above it, repeating the pass in thousands of
 // workgroups costs more than one schedule kernel that writes the item list.
 constexpr int kMaxInlineScheduleExperts = 64;
+// Up to this many experts launches whose items span at least kInlineScheduleMinK of K (long
+// items) also look up their items in the kernel, four experts per lane.
+constexpr int kMaxInlineScheduleExpertsLongK = 4 * 64;
+constexpr int kInlineScheduleMinK = 1024;
 
 // Rows of expert e (offsets clamped to [0, R] and made monotone) and its first row.
 __device__ __forceinline__ int expert_rows(const Params &P, int e, int64_t &lo) {
@@ -74,13 +78,78 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 // same weights from L2, so they keep the default policy).
 constexpr int kLastChunkFlag = 1 << 30;
 
+// The in-kernel lookup below for up to 4 * 64 experts (launches with long work items, where
+// one round trip per workgroup costs less than a schedule launch): lane l covers experts
+// 4l .. 4l + 3, whose five offsets it loads together (indices clamped to E: the array has
+// E + 1 entries); then the same wave-wide scan and owner lane as for one expert per lane.
+__device__ __forceinline__ bool item_for_block_4(const Params &P, int b, int4 &item, bool &last) {
+  const int jx = b / kXcds;
+  const int lane = threadIdx.x & 63;
+  const int cr = P.chunk_rows;
+  int32_t o[5];
+#pragma unroll
+  for (int q = 0; q < 5; q++) o[q] = P.offsets[min(4 * lane + q, P.E)];
+  int rows[4], lo[4], chunks[4];
+  int mine = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    int64_t l = o[q];
+    l = l < 0 ? 0 : (l > P.R ? P.R : l);
+    int64_t h = o[q + 1];
+    h = h < l ? l : (h > P.R ? P.R : h);
+    const bool valid = 4 * lane + q < P.E;
+    rows[q] = valid ? static_cast<int>(h - l) : 0;
+    lo[q] = static_cast<int>(l);
+    chunks[q] = (rows[q] + cr - 1) / cr;
+    mine += chunks[q] * P.n_tiles;
+  }
+  const int incl = wave_inclusive_scan(mine);
+  const int count = __builtin_amdgcn_readlane(incl, kWave - 1);
+  const int per_xcd = (count + kXcds - 1) / kXcds;
+  const int w = (b % kXcds) * per_xcd + jx;
+  if (jx >= per_xcd || w >= count) return false;
+  const int local = w - (incl - mine);
+  const uint64_t owner = __ballot(mine > 0 && local >= 0 && local < mine);
+  const int src = __builtin_ctzll(owner);
+  int l_src = __builtin_amdgcn_readlane(local, src);
+  // which of the owner's four experts (scalar: everything derived from the item stays uniform)
+  int e = 4 * src, c_src = 0, rows_src = 0, lo_src = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int cq = __builtin_amdgcn_readlane(chunks[q], src);
+    const int rq = __builtin_amdgcn_readlane(rows[q], src);
+    const int lq = __builtin_amdgcn_readlane(lo[q], src);
+    const int items_q = cq * P.n_tiles;
+    if (c_src == 0) {
+      if (l_src < items_q) {
+        e = 4 * src + q;
+        c_src = cq;
+        rows_src = rq;
+        lo_src = lq;
+      } else {
+        l_src -= items_q;
+      }
+    }
+  }
+  const int nt = l_src / c_src, c = l_src % c_src;
+  const int nr = rows_src - c * cr;
+  item = make_int4(e, lo_src + c * cr, nr < cr ? nr : cr, nt);
+  last = c == c_src - 1;
+  return true;
+}
+
 // Work item of workgroup b, or false if it has none; `last` is true for the last row chunk
 // of the item's expert.  Workgroup b runs on XCD b % 8, so
 // the items are dealt to XCDs in contiguous ranges: neighbouring items (the n tiles and row
 // chunks of one expert) share that XCD's L2.  The result is wave-uniform.  Without an item
 // list (at most kMaxInlineScheduleExperts = 64 experts) lane e reads the offsets of expert e
-// once and the wave derives the count and the item from them in one pass.
+// once and the wave derives the count and the item from them in one pass; up to
+// kMaxInlineScheduleExpertsLongK experts each lane takes four (item_for_block_4), in kernels
+// built with kFourPerLane (the K-split kernel is not: it looks up an item per loop trip, and
+// the larger lookup there costs it registers and time).
 static_assert(kMaxInlineScheduleExperts <= kWave, "inline scheduling keeps one expert per lane");
+static_assert(kMaxInlineScheduleExpertsLongK <= 4 * kWave, "the long-K lookup keeps four experts per lane");
+template <bool kFourPerLane = true>
 __device__ __forceinline__ bool item_for_block(const Params &P, int b, int4 &item, bool &last) {
   const int jx = b / kXcds;
   if (P.items) {
@@ -95,6 +164,7 @@ __device__ __forceinline__ bool item_for_block(const Params &P, int b, int4 &ite
   }
   const int lane = threadIdx.x & 63;
   const int cr = P.chunk_rows;
+  if (kFourPerLane && P.E > kWave) return item_for_block_4(P, b, item, last);
   int64_t lo = 0;
   int rows = 0, chunks = 0;
   if (lane < P.E) {

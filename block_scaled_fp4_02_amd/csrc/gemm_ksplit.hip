@@ -259,7 +259,7 @@ __global__ __launch_bounds__(64 * split_waves<KS>(), 8 / split_waves<KS>()) void
   for (int vb = blockIdx.x;; vb += gridDim.x) {   // a multiple of 8 apart: the same XCD
     int4 item;
     bool last;
-    if (!item_for_block(P, vb, item, last)) break;
+    if (!item_for_block<false>(P, vb, item, last)) break;
     float m;
     if (last) m = item.z <= 16 ? ks_body<1, KS, EPI, true>(P, red, item.x, item.y, item.z, item.w)
                                : ks_body<2, KS, EPI, true>(P, red, item.x, item.y, item.z, item.w);

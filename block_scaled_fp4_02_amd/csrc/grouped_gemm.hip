@@ -11,7 +11,8 @@
 //
 // Design (not the pages' SM120 tiles; this is for gfx950):
 //  * Work list: items (expert, row chunk, n tile), ordered expert-major, then n tile, then
-//    chunk; the last chunk of an expert is flagged (its weight loads are non-temporal).  Up to 64 experts every wave derives its own item from expert_offsets (a
+//    chunk; the last chunk of an expert is flagged (its weight loads are non-temporal).  Up to 64 experts (256 when K >= 1024, where items are long enough
+//    to absorb the lookup, except in the K-split kernel) every wave derives its own item from expert_offsets (a
 //    wave-wide sum and scan, no extra launch); above that a schedule kernel writes the list
 //    first (each of its workgroups scans the offsets and writes a slice of the items).  The grid is the host-side upper bound on the
 //    item count; items past the device-side count exit.
@@ -203,7 +204,8 @@ GemmPlan plan_gemm(const moe_gemm_args &a) {
     const int64_t resident = static_cast<int64_t>(256) * (8 / ksplit_waves(p.ks));
     p.grid = std::min<int64_t>(p.grid, resident);
   }
-  p.inline_schedule = a.E <= kMaxInlineScheduleExperts;
+  p.inline_schedule = a.E <= kMaxInlineScheduleExperts ||
+                      (a.E <= kMaxInlineScheduleExpertsLongK && a.K >= kInlineScheduleMinK && p.kernel != kKSplit);
   p.ws_bytes = p.inline_schedule ? 16 : 16 + static_cast<size_t>(p.max_items) * sizeof(int4);
   return p;
 }

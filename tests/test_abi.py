@@ -146,10 +146,19 @@ def test_single_step_items_cover_several_n_tiles():
 
 
 def test_gemm_workspace_grows_with_rows_and_experts():
+    """Launches whose items are looked up in the kernel need only the 16-byte item count (up
+    to 64 experts, or up to 256 with K >= 1024 outside the K-split kernel); the others hold
+    an item list that grows with the rows and the experts."""
     L = moe.lib()
-    small = L.moe_grouped_gemm_nvfp4_workspace(C.byref(gemm_args(E=8, R=256)))
-    big = L.moe_grouped_gemm_nvfp4_workspace(C.byref(gemm_args(E=256, R=131072)))
-    assert big > small > 0
+    ws = lambda layout=0, **kw: L.moe_grouped_gemm_nvfp4_workspace(C.byref(gemm_args(layout=layout, **kw)))
+    assert ws(E=8, R=256) == 16
+    assert ws(E=256, R=131072) == 16
+    assert ws(E=256, R=8192, K=7168, N=512, layout=1) == 16
+    assert ws(E=256, R=8192, K=512, layout=1) > 16
+    assert ws(E=257, R=131072) > ws(E=257, R=8192) > 16
+    assert ws(E=256, R=131072, K=256) > ws(E=256, R=8192, K=256) > 16
+    # 100 experts whose few rows leave the K-split kernel in charge: listed items
+    assert ws(E=100, R=139, K=2048, N=256, layout=1) > 16
 
 
 def test_finalize_validation():

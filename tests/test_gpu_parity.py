@@ -258,6 +258,9 @@ def _run_gemm_none(A, Bs, off, A_rows, R, label, packed=False):
     ([20, 7, 32], 4096, 256, True),                       # K split 8 ways, 5 and 3 half steps per wave
     ([33] * 32, 512, 2048, False),                        # K split 2 ways: 1024 items looped over 512 workgroups
     ([1] * 60 + [0, 40, 2] + [1] * 37, 2048, 256, True),  # 100 experts, K split 8 ways: listed items looped
+    ([1] * 60 + [0, 40, 2] + [1] * 37, 512, 256, True),   # 100 experts, K split 2 ways: listed items looped
+    ([0, 3, 17, 48, 49, 1] * 42 + [5, 0, 60, 2], 1024, 1024, True),  # 256 experts, four-wave kernel, in-kernel lookup
+    ([96, 130, 0, 250, 97] * 40, 1024, 512, False),       # 200 experts, eight-wave kernel, in-kernel lookup
     ([0, 1, 2, 3, 5, 8, 13] * 150 + [40, 0], 256, 256, True),  # 1052 experts: two scan blocks in the schedule
     ([0, 0, 0], 256, 256, False),                         # no rows at all
     ([300], 256, 768, True),                              # one big group: several row chunks
