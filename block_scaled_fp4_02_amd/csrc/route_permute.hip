@@ -20,6 +20,9 @@
 //                      in expert e's group within the chunk is the popcount of the bits
 //                      below t, which is the stable order t*k + j because a token names
 //                      each expert at most once.
+//   count_scatter_kernel  up to kFusedMaxTokens tokens: the scatter without the count
+//                      launch -- each workgroup histograms all T*k ids in LDS (all rows, and
+//                      the rows of earlier chunks) and takes its bases from that.
 #include "common.hpp"
 
 
@@ -157,38 +160,15 @@ __global__ __launch_bounds__(kChunk) void chunk_count_kernel(const int32_t *__re
   }
 }
 
-// Per workgroup (chunk c): base[e] = expert_offsets[e] + (rows of expert e in chunks < c),
-// from the read-only chunk counts -- a column sum per expert, then an exclusive scan over
+constexpr int kPer = kMaxE / kChunk;   // experts per thread in the scans below
+
+// base[e] = expert_offsets[e] + before[e] from each expert's total rows and rows in earlier
+// chunks (thread t holds experts t * kPer .. + kPer): an exclusive scan of the totals over
 // experts.  Workgroup 0 also writes expert_offsets.
-__device__ __forceinline__ void chunk_bases(const int32_t *__restrict__ counts, int nchunks, int E, int chunk,
-                                            int32_t *base, int32_t *wave_total,
-                                            int32_t *__restrict__ offsets) {
+__device__ __forceinline__ void bases_from_totals(int (&total)[kPer], int (&before)[kPer], int E, int chunk,
+                                                  int32_t *base, int32_t *wave_total,
+                                                  int32_t *__restrict__ offsets) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  constexpr int kPer = kMaxE / kChunk;   // experts per thread
-  constexpr int kBatch = 8;              // chunks whose counts are loaded together
-  int total[kPer], before[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; i++) total[i] = before[i] = 0;
-  // consecutive experts per thread keep the scan simple; every load of a batch is issued
-  // before any is summed (indices clamped into the table, out-of-range terms dropped)
-  for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
-    int n[kPer][kBatch];
-#pragma unroll
-    for (int i = 0; i < kPer; i++) {
-      const int e = min(t * kPer + i, E - 1);
-#pragma unroll
-      for (int u = 0; u < kBatch; u++)
-        n[i][u] = counts[static_cast<int64_t>(min(c0 + u, nchunks - 1)) * E + e];
-    }
-#pragma unroll
-    for (int i = 0; i < kPer; i++)
-#pragma unroll
-      for (int u = 0; u < kBatch; u++) {
-        const int c = c0 + u;
-        total[i] += c < nchunks ? n[i][u] : 0;
-        before[i] += c < chunk ? n[i][u] : 0;
-      }
-  }
   int mine = 0;
 #pragma unroll
   for (int i = 0; i < kPer; i++) {
@@ -218,16 +198,45 @@ __device__ __forceinline__ void chunk_bases(const int32_t *__restrict__ counts, 
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kChunk) void scatter_kernel(const int32_t *__restrict__ ids, int T, int E,
-                                                         int k, const int32_t *__restrict__ counts, int nchunks,
-                                                         int32_t *__restrict__ offsets,
-                                                         int32_t *__restrict__ row_src,
-                                                         int32_t *__restrict__ token_slot_row) {
-  __shared__ unsigned long long bm[kMaxE * kWords];
-  __shared__ int32_t base[kMaxE];
-  __shared__ int32_t wave_total[kChunk / 64];
-  chunk_bases(counts, nchunks, E, blockIdx.x, base, wave_total, offsets);
-  build_bitmaps(bm, ids, T, E, k, blockIdx.x);
+// Per workgroup (chunk c): base[e] = expert_offsets[e] + (rows of expert e in chunks < c),
+// from the read-only chunk counts -- a column sum per expert, then the scan above.
+__device__ __forceinline__ void chunk_bases(const int32_t *__restrict__ counts, int nchunks, int E, int chunk,
+                                            int32_t *base, int32_t *wave_total,
+                                            int32_t *__restrict__ offsets) {
+  const int t = threadIdx.x;
+  constexpr int kBatch = 8;              // chunks whose counts are loaded together
+  int total[kPer], before[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; i++) total[i] = before[i] = 0;
+  // consecutive experts per thread keep the scan simple; every load of a batch is issued
+  // before any is summed (indices clamped into the table, out-of-range terms dropped)
+  for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+    int n[kPer][kBatch];
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      const int e = min(t * kPer + i, E - 1);
+#pragma unroll
+      for (int u = 0; u < kBatch; u++)
+        n[i][u] = counts[static_cast<int64_t>(min(c0 + u, nchunks - 1)) * E + e];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; i++)
+#pragma unroll
+      for (int u = 0; u < kBatch; u++) {
+        const int c = c0 + u;
+        total[i] += c < nchunks ? n[i][u] : 0;
+        before[i] += c < chunk ? n[i][u] : 0;
+      }
+  }
+  bases_from_totals(total, before, E, chunk, base, wave_total, offsets);
+}
+
+// Rows of this chunk's tokens: the rank of token t in expert e's rows within the chunk is the
+// popcount of the chunk bitmap's bits below t.
+__device__ __forceinline__ void scatter_chunk(const int32_t *__restrict__ ids, int T, int E, int k,
+                                              const unsigned long long *bm, const int32_t *base,
+                                              int32_t *__restrict__ row_src,
+                                              int32_t *__restrict__ token_slot_row) {
   const int t = blockIdx.x * kChunk + threadIdx.x;
   if (t >= T) return;
   const int word = threadIdx.x >> 6;
@@ -242,6 +251,70 @@ __global__ __launch_bounds__(kChunk) void scatter_kernel(const int32_t *__restri
     row_src[p] = t;
     token_slot_row[static_cast<int64_t>(t) * k + j] = static_cast<int32_t>(p);
   }
+}
+
+__global__ __launch_bounds__(kChunk) void scatter_kernel(const int32_t *__restrict__ ids, int T, int E,
+                                                         int k, const int32_t *__restrict__ counts, int nchunks,
+                                                         int32_t *__restrict__ offsets,
+                                                         int32_t *__restrict__ row_src,
+                                                         int32_t *__restrict__ token_slot_row) {
+  __shared__ unsigned long long bm[kMaxE * kWords];
+  __shared__ int32_t base[kMaxE];
+  __shared__ int32_t wave_total[kChunk / 64];
+  chunk_bases(counts, nchunks, E, blockIdx.x, base, wave_total, offsets);
+  build_bitmaps(bm, ids, T, E, k, blockIdx.x);
+  scatter_chunk(ids, T, E, k, bm, base, row_src, token_slot_row);
+}
+
+// Up to this many tokens the count launch is folded into the scatter: every workgroup reads
+// all T * k ids (at most 128 K ids, from L2) instead of a count table.
+constexpr int kFusedMaxTokens = 4096;
+
+__global__ __launch_bounds__(kChunk) void count_scatter_kernel(const int32_t *__restrict__ ids, int T, int E,
+                                                               int k, int32_t *__restrict__ offsets,
+                                                               int32_t *__restrict__ row_src,
+                                                               int32_t *__restrict__ token_slot_row) {
+  __shared__ unsigned long long bm[kMaxE * kWords];
+  __shared__ int32_t base[kMaxE];
+  __shared__ int32_t hist_all[kMaxE];
+  __shared__ int32_t hist_before[kMaxE];
+  __shared__ int32_t wave_total[kChunk / 64];
+  const int t = threadIdx.x;
+  for (int e = t; e < E; e += kChunk) hist_all[e] = hist_before[e] = 0;
+  __syncthreads();
+  // rows per expert over all tokens, and over the tokens of earlier chunks (ids before
+  // index `cut`); integer counts, so the order of the LDS additions does not matter
+  const int64_t n = static_cast<int64_t>(T) * k;
+  const int64_t cut = static_cast<int64_t>(blockIdx.x) * kChunk * k;
+  constexpr int kBatch = 8;   // id loads issued together per thread
+  for (int64_t i0 = 0; i0 < n; i0 += kBatch * kChunk) {
+    int32_t v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) {
+      const int64_t i = i0 + u * kChunk + t;
+      v[u] = ids[i < n ? i : n - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) {
+      const int64_t i = i0 + u * kChunk + t;
+      if (i < n) {
+        const int e = clamp_expert(v[u], E);
+        atomicAdd(&hist_all[e], 1);
+        if (i < cut) atomicAdd(&hist_before[e], 1);
+      }
+    }
+  }
+  __syncthreads();
+  int total[kPer], before[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; i++) {
+    const int e = min(t * kPer + i, E - 1);
+    total[i] = hist_all[e];
+    before[i] = hist_before[e];
+  }
+  bases_from_totals(total, before, E, blockIdx.x, base, wave_total, offsets);
+  build_bitmaps(bm, ids, T, E, k, blockIdx.x);
+  scatter_chunk(ids, T, E, k, bm, base, row_src, token_slot_row);
 }
 
 // No tokens: every group is empty.
@@ -268,10 +341,15 @@ hipError_t launch_route_permute(const float *logits, int T, int E, int k, int32_
     else if (E <= 256) hipLaunchKernelGGL(topk_kernel<4>, tg, tb, 0, stream, logits, T, E, k, topk_ids, topk_w);
     else if (E <= 512) hipLaunchKernelGGL(topk_kernel<8>, tg, tb, 0, stream, logits, T, E, k, topk_ids, topk_w);
     else hipLaunchKernelGGL(topk_kernel<kMaxPerLane>, tg, tb, 0, stream, logits, T, E, k, topk_ids, topk_w);
-    hipLaunchKernelGGL(chunk_count_kernel, dim3(nchunks), dim3(kChunk), 0, stream, topk_ids, T, E,
-                       k, counts);
-    hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(kChunk), 0, stream, topk_ids, T, E, k,
-                       counts, nchunks, expert_offsets, row_src, token_slot_row);
+    if (T <= kFusedMaxTokens) {
+      hipLaunchKernelGGL(count_scatter_kernel, dim3(nchunks), dim3(kChunk), 0, stream, topk_ids, T, E, k,
+                         expert_offsets, row_src, token_slot_row);
+    } else {
+      hipLaunchKernelGGL(chunk_count_kernel, dim3(nchunks), dim3(kChunk), 0, stream, topk_ids, T, E,
+                         k, counts);
+      hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(kChunk), 0, stream, topk_ids, T, E, k,
+                         counts, nchunks, expert_offsets, row_src, token_slot_row);
+    }
   } else {
     hipLaunchKernelGGL(zero_offsets_kernel, dim3(1), dim3(kMaxE), 0, stream, E, expert_offsets);
   }

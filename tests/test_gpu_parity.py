@@ -96,7 +96,10 @@ def test_route_permute_workloads(L):
 
 @pytest.mark.parametrize("T,E,k", [(0, 8, 2), (1, 1, 1), (37, 1024, 32), (100, 8, 8), (300, 3, 2), (257, 256, 8),
                                    (50, 100, 4), (40, 300, 6), (33, 513, 8), (65, 64, 3), (129, 128, 2),
-                                   (2305, 160, 8)])   # 1..16 logits per lane; 10 chunks (two count batches)
+                                   # 10 chunks, and the largest batch whose workgroups histogram all
+                                   # ids themselves; then 17 chunks through the count table (three
+                                   # count batches, a one-token last chunk)
+                                   (2305, 160, 8), (4096, 256, 8), (4097, 160, 8)])   # 1..16 logits per lane
 def test_route_permute_edges(T, E, k):
     rng = np.random.default_rng(T * 7 + E + k)
     logits = rng.standard_normal((T, E)).astype(np.float32)
