@@ -93,12 +93,13 @@ def copy_calibration(mib: int):
 _probe = None
 
 
-def stream_probe():
-    """The streaming-read measurement kernel (block_scaled_fp4_02_amd/libmoe_stream_probe.so)."""
+def probes():
+    """The measurement kernels, streaming read and MFMA throughput
+    (block_scaled_fp4_02_amd/libmoe_probes.so)."""
     global _probe
     if _probe is None:
         import ctypes as C
-        path = os.path.join(ROOT, "block_scaled_fp4_02_amd", "libmoe_stream_probe.so")
+        path = os.path.join(ROOT, "block_scaled_fp4_02_amd", "libmoe_probes.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
         L = C.CDLL(path)
@@ -109,25 +110,75 @@ def stream_probe():
         L.moe_probe_stream_read_groups.argtypes = [C.c_int64, C.c_int, C.c_int64]
         L.moe_probe_stream_read.restype = C.c_int
         L.moe_probe_stream_read.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_int64, C.c_void_p, C.c_void_p]
+        L.moe_probe_mfma_kinds.restype = C.c_int
+        L.moe_probe_mfma_flops_per_wave_iter.restype = C.c_double
+        L.moe_probe_mfma_flops_per_wave_iter.argtypes = [C.c_int]
+        L.moe_probe_mfma_expected_sink.restype = C.c_double
+        L.moe_probe_mfma_expected_sink.argtypes = [C.c_int, C.c_int]
+        L.moe_probe_mfma_peak.restype = C.c_int
+        L.moe_probe_mfma_peak.argtypes = [C.c_int, C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
         _probe = L
     return _probe
+
+
+MFMA_KINDS = ("f16_16x16x32", "fp4_16x16x128")
+
+
+def mfma_peak(torch, iters: int = 2048, launches: int = 5) -> dict:
+    """Measured dense MFMA throughput per kind (fp16 16x16x32, FP4 16x16x128 with unit block
+    scales): back-to-back MFMAs on register operands over 4, 8 or 16 workgroups of four waves
+    per CU, HIP events on the launch stream; the fastest grid is the measured peak at the
+    clock the board holds under that load.  Each launch's sums are checked against their
+    exact value."""
+    import ctypes as C
+    L = probes()
+    stream = torch.cuda.current_stream()
+    sp = C.c_void_p(stream.cuda_stream)
+    out = {}
+    for kind, name in enumerate(MFMA_KINDS):
+        best = None
+        for groups in (256 * 4, 256 * 8, 256 * 16):
+            sink = torch.empty(groups * 4, dtype=torch.float32, device="cuda")
+
+            def launch():
+                rc = L.moe_probe_mfma_peak(kind, groups, iters, C.c_void_p(sink.data_ptr()), sp)
+                if rc != 0:
+                    raise RuntimeError(f"moe_probe_mfma_peak: hipError {rc}")
+            launch()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(launches):
+                launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            want = L.moe_probe_mfma_expected_sink(kind, iters)
+            if not bool((sink == want).all()):
+                raise RuntimeError(f"MFMA probe {name}: sums differ from {want}")
+            us = e0.elapsed_time(e1) * 1e3 / launches
+            tf = groups * 4 * L.moe_probe_mfma_flops_per_wave_iter(kind) * iters / (us * 1e-6) / 1e12
+            if best is None or tf > best["TFLOPs"]:
+                best = {"TFLOPs": round(tf, 1), "avg_launch_us": round(us, 1), "workgroups": groups,
+                        "workgroups_per_cu": groups // 256}
+        out[name] = best
+    return out
 
 
 def stream_read(torch, nbytes: int, copies: int, launches: int) -> dict:
     """The streaming-read kernel over one of `copies` distinct buffers of `nbytes` each, cycled
     (together larger than the 256 MB of on-die cache when copies > 1, so every launch reads
     HBM), HIP events on the launch stream.  Every variant (loads in flight per lane, cache
-    policy) and grid (one round over the buffer, or 2, 4 or 8 looping workgroups per CU) is
+    policy) and grid (one round over the buffer, or 1, 2, 4 or 8 looping workgroups per CU) is
     timed; the fastest is the measured read rate at this size."""
     import ctypes as C
-    L = stream_probe()
+    L = probes()
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(copies)]
     sink = torch.empty(4 * (1 << 19), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
     sp = C.c_void_p(stream.cuda_stream)
     best = None
     for v in range(L.moe_probe_stream_read_variants()):
-        for max_groups in (1 << 19, 256 * 8, 256 * 4, 256 * 2):
+        for max_groups in (1 << 19, 256 * 8, 256 * 4, 256 * 2, 256):
             groups = int(L.moe_probe_stream_read_groups(nbytes, v, max_groups))
 
             def launch(i):
@@ -610,9 +661,24 @@ def main():
         mm = torch_f16_matmul_tflops(torch)
         rec["roofline"]["measured_f16_matmul_TFLOPs"] = round(mm, 1)
         rec["roofline"]["frac_of_measured_f16_matmul"] = round(rec["roofline"]["achieved"] / mm, 4)
+        mp = mfma_peak(torch)
+        rec["measured_mfma_peak"] = mp
+        rec["roofline"]["measured_f16_mfma_TFLOPs"] = mp["f16_16x16x32"]["TFLOPs"]
+        rec["roofline"]["frac_of_measured_f16_mfma"] = round(
+            rec["roofline"]["achieved"] / mp["f16_16x16x32"]["TFLOPs"], 4)
     if L is synth.LAYER_DECODE and extras:
         rec["grouped_gemm_decode_8x32"] = grouped_gemm_decode(moe, torch, args.steps)
         rec["dense_gemm_8192"] = dense_gemm(moe, torch)
+        # measured companions to the spec MFMA peaks, for the MFMA-bound records above
+        mp = mfma_peak(torch)
+        rec["measured_mfma_peak"] = mp
+        f16 = mp["f16_16x16x32"]["TFLOPs"]
+        pr = rec["layer_prefill"]["roofline"]
+        pr["measured_f16_mfma_TFLOPs"] = f16
+        pr["frac_of_measured_f16_mfma"] = round(pr["achieved"] / f16, 4)
+        pr["frac_of_measured_fp4_mfma"] = round(pr["achieved"] / mp["fp4_16x16x128"]["TFLOPs"], 4)
+        dg = rec["dense_gemm_8192"]
+        dg["frac_of_measured_f16_mfma"] = round(dg["tflops"] / f16, 4)
         for key, Ls in (("shard_ep8", synth.LAYER_EP8), ("shard_tp8", synth.LAYER_TP8)):
             rec[key] = shard_record(Ls, moe, torch, args.steps)
             del rec[key]["offsets"]

@@ -18,9 +18,13 @@ BUILD_DIR = os.path.join(ROOT, "_build", "moe_nvfp4")
 LIB_PATH = os.path.join(PKG, "libmoe_nvfp4.so")
 SOURCES = ["route_permute.hip", "quantize.hip", "grouped_gemm.hip", "gemm_lds.hip", "gemm_ksplit.hip",
            "gemm_rowmajor.hip", "finalize.hip", "moe_api.hip"]
-# the benchmark's streaming-read measurement kernel, a library of its own (not the MoE ABI)
-PROBE_SOURCES = ["stream_probe.hip"]
-PROBE_LIB_PATH = os.path.join(PKG, "libmoe_stream_probe.so")
+# the benchmark's measurement kernels (streaming read, MFMA throughput), a library of their own
+# (not the MoE ABI)
+PROBE_SOURCES = ["stream_probe.hip", "mfma_probe.hip"]
+PROBE_LIB_PATH = os.path.join(PKG, "libmoe_probes.so")
+# per-source extra flags: the MFMA probe's loop keeps its accumulators in VGPRs only in the
+# VGPR form of MFMA
+EXTRA_FLAGS = {"mfma_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH_FLAGS = ["--offload-arch=gfx950"]
@@ -31,7 +35,7 @@ COMPILE_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *ARCH_FLAGS, *COMPILE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *ARCH_FLAGS, *COMPILE_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 target feature and says so: harmless.
     noise = "is not a recognized feature for this target"
