@@ -292,10 +292,11 @@ def grouped_gemm_decode(moe, torch, steps: int, copies: int = 8, with_stream_rea
     D = torch.empty(R, G.N, dtype=torch.bfloat16, device=dev)
     args = [moe._gemm_args_for(A, W, off, R, moe.MOE_EPI_NONE, D, None) for W in Ws]
     ws = moe._ws(moe.moe_grouped_gemm_nvfp4_workspace(args[0]), dev)
-    for a in args:
-        moe.moe_grouped_gemm_nvfp4(a, ws)
+    for _ in range(2):   # warm-up: every copy twice (16 launches)
+        for a in args:
+            moe.moe_grouped_gemm_nvfp4(a, ws)
     torch.cuda.synchronize()
-    n = max(steps, 10) * copies
+    n = max(steps, 13) * copies   # at least 100 timed launches
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(n):
