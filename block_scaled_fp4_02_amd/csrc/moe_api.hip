@@ -3,6 +3,7 @@
 // caller's stream.  No entry point allocates, synchronises or throws.
 #include "common.hpp"
 
+#include <cstring>
 #include <mutex>
 
 namespace moe {
@@ -62,9 +63,10 @@ moe_status check_gemm(const moe_gemm_args *a, bool need_pointers) {
   if (a->K % 256 != 0 || a->N % 256 != 0) return MOE_ERR_UNSUPPORTED;
   if (a->R > 0 && a->rows_A < 1) return MOE_ERR_SHAPE;
   // the packed kernel addresses the activation codes and each expert's packed weights
-  // through 32-bit range-checked buffer descriptors
+  // through 32-bit range-checked buffer descriptors (K >= 256 here; the bound on rows_A is
+  // tested by division, so that no product can overflow)
   if (a->B_layout == MOE_LAYOUT_PACKED &&
-      (a->rows_A * (a->K / 2) > kMaxPackedBufBytes || static_cast<int64_t>(a->N) * a->K / 16 * 9 > kMaxPackedBufBytes))
+      (a->rows_A > kMaxPackedBufBytes / (a->K / 2) || static_cast<int64_t>(a->N) * a->K / 16 * 9 > kMaxPackedBufBytes))
     return MOE_ERR_UNSUPPORTED;
   // item indices, row indices and workgroup counts stay in 32 bits
   const GemmPlan plan = plan_gemm(*a);
@@ -88,7 +90,11 @@ using namespace moe;
 extern "C" {
 
 const char *moe_status_string(moe_status s) {
-  switch (s) {
+  // a C caller may pass any int: read the bits rather than the enum value, which C++ only
+  // defines within the enumerators' range
+  int v = 0;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case MOE_OK: return "ok";
     case MOE_ERR_NULL: return "a required pointer is NULL";
     case MOE_ERR_SHAPE: return "a size is negative, inconsistent or out of range";

@@ -103,6 +103,12 @@ def test_gemm_can_implement_is_truthful_on_shapes():
         assert L.moe_grouped_gemm_nvfp4_can_implement(C.byref(a)) == want, kw
         assert L.moe_grouped_gemm_nvfp4(C.byref(a), FAKE, 1 << 30, None) == want, kw
     assert L.moe_grouped_gemm_nvfp4_can_implement(None) == moe.MOE_ERR_NULL
+    # activation rows beyond the packed kernel's 32-bit descriptors are refused, also where
+    # rows_A * K / 2 would wrap around 2^64
+    for rows_a in (2 ** 31 // 128, 2 ** 57, 2 ** 63 - 1):
+        a = gemm_args(layout=1, K=256)
+        a.rows_A = rows_a
+        assert L.moe_grouped_gemm_nvfp4_can_implement(C.byref(a)) == moe.MOE_ERR_UNSUPPORTED, rows_a
     # SwiGLU + NVFP4 with packed weights and all its pointers is supported
     assert L.moe_grouped_gemm_nvfp4_can_implement(C.byref(gemm_args(epi=2, layout=1))) == moe.MOE_OK
     # amax_out is only needed by the SwiGLU epilogue
