@@ -45,8 +45,8 @@ struct Params {
 };
 
 // Largest expert count for which waves derive their work item from the offsets themselves
-// (one wave-wide pass, an expert per lane); above it, repeating the pass in thousands of
-// workgroups costs more than one schedule kernel that writes the item list.
+// (one wave-wide pass, an expert per lane); above it, for short items, repeating the pass in
+// thousands of workgroups costs more than one schedule kernel that writes the item list.
 constexpr int kMaxInlineScheduleExperts = 64;
 // Up to this many experts launches whose items span at least kInlineScheduleMinK of K (long
 // items) also look up their items in the kernel, four experts per lane.

@@ -11,11 +11,13 @@
 //
 // Design (not the pages' SM120 tiles; this is for gfx950):
 //  * Work list: items (expert, row chunk, n tile), ordered expert-major, then n tile, then
-//    chunk; the last chunk of an expert is flagged (its weight loads are non-temporal).  Up to 64 experts (256 when K >= 1024, where items are long enough
-//    to absorb the lookup, except in the K-split kernel) every wave derives its own item from expert_offsets (a
-//    wave-wide sum and scan, no extra launch); above that a schedule kernel writes the list
-//    first (each of its workgroups scans the offsets and writes a slice of the items).  The grid is the host-side upper bound on the
-//    item count; items past the device-side count exit.
+//    chunk; the last chunk of an expert is flagged (its weight loads are non-temporal).
+//    Up to 64 experts (256 when K >= 1024, where items are long enough to absorb the
+//    lookup, except in the K-split kernel) every wave derives its own item from
+//    expert_offsets (a wave-wide sum and scan, no extra launch); above that a schedule
+//    kernel writes the list first (each of its workgroups scans the offsets and writes a
+//    slice of the items).  The grid is the host-side upper bound on the item count; items
+//    past the device-side count exit.
 //  * Per-shape plan (the counterpart of the pages' tile table, chosen from host-known sizes
 //    only, so a supported launch cannot fail on its configuration):
 //      packed weights, >= 96 rows per expert       -> wide LDS kernel, 96-row chunks, 512-row n tiles

@@ -659,8 +659,9 @@ def test_layer_deterministic():
 def test_layer_deterministic_full_size(L):
     """The benchmark's kernel paths at full size, run three times on the same inputs with the
     outputs overwritten in between: every intermediate is identical byte for byte.  Decode:
-    the schedule kernel and the four-wave LDS kernels; TP8 share: items of several n tiles
-    (K = 256); prefill: the eight-wave kernel over ~512 rows per expert."""
+    the four-wave LDS kernels with their items looked up in the kernel (256 experts, four per
+    lane); TP8 share: the schedule kernel and items of several n tiles (K = 256); prefill:
+    the eight-wave kernel over ~512 rows per expert."""
     _, _, d1, d2 = layer_weights(L)
     plan = moe.MoELayerPlan(L.T, L.E, L.k, L.H, L.I, d1, d2)
     logits, x = dev(synth.router_logits(L)), dev_bf16(synth.layer_activations(L))
