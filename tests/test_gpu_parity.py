@@ -336,20 +336,24 @@ def test_gemm_none_decode_grouped_gemm_full(packed):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("E,N,K,rows", [
+@pytest.mark.parametrize("E,N,K,rows,packed", [
     # four-wave kernel: each expert's packed weights just under the 2^31-byte reach of its
     # 32-bit buffer descriptor (2,146,959,360 B), the second expert starting past 2^31 bytes
-    (2, 116480, 32768, 16),
+    (2, 116480, 32768, 16, True),
     # eight-wave kernel (>= 96 rows per expert, N % 512 == 0), likewise at the limit
-    (2, 116224, 32768, 100),
+    (2, 116224, 32768, 100, True),
     # K-split kernel: one 256-row expert with 7281 K steps of 2048 (2,147,254,272 B)
-    (1, 256, 14911488, 16),
-], ids=["four_wave", "eight_wave", "k_split"])
-def test_gemm_largest_packed_experts(E, N, K, rows):
-    """The largest experts the packed kernels address: random codes and scales (every E2M1
-    code, E4M3 scales 0.5-1.875), NONE epilogue, the first and last row of every expert
-    against the oracle's rows (all N columns each)."""
-    assert moe.lib().moe_pack_weights_nvfp4_bytes(N, K) <= (1 << 31) - 4096
+    (1, 256, 14911488, 16, True),
+    # row-major weights (64-bit addressing, no such limit): 4.3 GB of codes, the second
+    # expert starting past 2^32 bytes
+    (2, 131072, 32768, 16, False),
+], ids=["four_wave", "eight_wave", "k_split", "row_major"])
+def test_gemm_largest_experts(E, N, K, rows, packed):
+    """The largest experts the kernels address: random codes and scales (every E2M1 code,
+    E4M3 scales 0.5-1.875), NONE epilogue, the first and last row of every expert against
+    the oracle's rows (all N columns each)."""
+    if packed:
+        assert moe.lib().moe_pack_weights_nvfp4_bytes(N, K) <= (1 << 31) - 4096
     rng = np.random.default_rng(N + K + rows)
     R = E * rows
     log(f"gemm NONE largest experts: E={E} N={N} K={K} rows={rows}: generating")
@@ -360,7 +364,9 @@ def test_gemm_largest_packed_experts(E, N, K, rows):
                      rng.integers(0x30, 0x40, (R, K // 16), dtype=np.uint8), 1.0 / 8)
     off = np.arange(0, R + 1, rows, dtype=np.int32)
     dA = moe.NVFP4Tensor(dev(A.q), dev(A.sf), dev(np.array([A.g], np.float32)))
-    dB = moe.pack_weights(moe.NVFP4Tensor(dev(Bq), dev(Bsf), dev(gB)))
+    dB = moe.NVFP4Tensor(dev(Bq), dev(Bsf), dev(gB))
+    if packed:
+        dB = moe.pack_weights(dB)
     torch.cuda.synchronize()
     log("gemm NONE largest experts: GPU")
     D = moe.grouped_gemm_alloc(dA, dB, dev(off), R, moe.MOE_EPI_NONE)
@@ -371,7 +377,7 @@ def test_gemm_largest_packed_experts(E, N, K, rows):
     torch.cuda.empty_cache()
     log(f"gemm NONE largest experts: oracle rows {sample.tolist()}")
     ref = oracle.grouped_gemm(A, Bq, Bsf, gB, off, rows=sample)
-    check_bf16(got, ref, f"gemm NONE largest experts E={E} N={N} K={K}")
+    check_bf16(got, ref, f"gemm NONE largest experts E={E} N={N} K={K} {'packed' if packed else 'row-major'}")
 
 
 def test_gemm_dense_small_full():
