@@ -496,6 +496,16 @@ def run_layer(L, moe, torch, steps: int, warmup: int, weights=None, fused: bool 
         plan.forward(logits, x)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    # the same steps replayed from a HIP graph of one forward pass (no host launch work)
+    g = plan.graph(logits, x)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    del g
 
     off = plan.off.cpu().numpy()
     sizes = np.diff(off)
@@ -512,7 +522,7 @@ def run_layer(L, moe, torch, steps: int, warmup: int, weights=None, fused: bool 
     g2_s = stage_us["gemm2"] * 1e-6
     weight_gbps = (w1_bytes + w2_bytes) / (g1_s + g2_s) / 1e9
     return {"plan": plan, "weights": (W1, W2), "off": off, "sizes": sizes, "ms_per_step": ms_per_step,
-            "stage_us": stage_us,
+            "graph_ms_per_step": graph_ms_per_step, "stage_us": stage_us,
             "value": (gemm1_flops + gemm2_flops) / (ms_per_step * 1e-3) / 1e12,
             "gemm_tflops": (gemm1_flops + gemm2_flops) / (g1_s + g2_s) / 1e12,
             "weight_gbps": weight_gbps, "g1_alg_bytes": g1_alg_bytes, "g1_s": g1_s, "g1_flops": gemm1_flops}
@@ -546,7 +556,8 @@ def shard_record(L, moe, torch, steps: int, weights=None) -> dict:
     under expert or tensor parallelism, or the skewed decode layer); `weights` reuses packed
     weights of the same shape."""
     r = run_layer(L, moe, torch, steps, 2, weights=weights)
-    out = {"workload": L.name, "ms_per_step": round(r["ms_per_step"], 4), "tflops": round(r["value"], 2),
+    out = {"workload": L.name, "ms_per_step": round(r["ms_per_step"], 4),
+           "graph_ms_per_step": round(r["graph_ms_per_step"], 4), "tflops": round(r["value"], 2),
            "gemm_tflops": round(r["gemm_tflops"], 2), "weight_hbm_GBps": round(r["weight_gbps"], 1),
            "weight_hbm_frac": round(r["weight_gbps"] / HBM_PEAK_GBPS, 4),
            "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
@@ -565,6 +576,7 @@ def prefill_record(L, moe, torch, steps: int, weights) -> dict:
     tf1, tf2 = r["g1_flops"] / g1_s / 1e12, g2_flops / g2_s / 1e12
     sizes = r["sizes"]
     out = {"workload": L.name, "steps": steps, "ms_per_step": round(r["ms_per_step"], 4),
+           "graph_ms_per_step": round(r["graph_ms_per_step"], 4),
            "tflops": round(r["value"], 2), "gemm_tflops": round(r["gemm_tflops"], 2),
            "rows_per_expert_min_median_max": [int(sizes.min()), int(np.median(sizes)), int(sizes.max())],
            "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
@@ -626,6 +638,7 @@ def main():
                    "operands": "NVFP4 (e2m1, e4m3 scale per 16, f32 global) dequantised exactly to fp16 MFMA, fp32 accumulate",
                    "weights_layout": "packed"},
         "roofline": roofline_record(L, r),
+        "graph_ms_per_step": round(r["graph_ms_per_step"], 4),
         "gemm_tflops": round(r["gemm_tflops"], 2),
         "weight_hbm_GBps": round(r["weight_gbps"], 1),
         "weight_hbm_frac": round(r["weight_gbps"] / HBM_PEAK_GBPS, 4),
@@ -636,7 +649,8 @@ def main():
     if L is synth.LAYER_DECODE and extras:
         f = run_layer(L, moe, torch, args.steps, args.warmup, weights=r["weights"], fused=True)
         rec["layer_decode_fused_static_g2"] = {
-            "ms_per_step": round(f["ms_per_step"], 4), "tflops": round(f["value"], 2),
+            "ms_per_step": round(f["ms_per_step"], 4), "graph_ms_per_step": round(f["graph_ms_per_step"], 4),
+            "tflops": round(f["value"], 2),
             "stage_us": {k: round(v, 2) for k, v in f["stage_us"].items()},
             "note": "SwiGLU output requantised in the gate/up GEMM epilogue (MOE_EPI_SWIGLU_NVFP4) with a "
                     "static global scale calibrated from one dynamic pass; requantize stage is empty"}

@@ -368,6 +368,21 @@ class MoELayerPlan:
         self.finalize(main)
         return self.out
 
+    def graph(self, logits, x) -> "torch.cuda.CUDAGraph":
+        """Capture one forward pass over the input buffers `logits` and `x` into a HIP graph
+        (both streams: the quantiser's branch forks from and joins the capture stream).
+        replay() reruns the whole layer on whatever those buffers hold at the time, writing
+        the same output buffers; a serving loop copies each batch into them first.  The pass
+        allocates nothing and records no memory-set node: every buffer is cleared or written
+        by the library's own kernels."""
+        self.forward(logits, x)              # one eager pass first (lazy initialisation)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(logits, x)
+        torch.cuda.synchronize()
+        return g
+
 
 def quantize_experts(W: torch.Tensor, stream=None) -> NVFP4Tensor:
     """NVFP4-quantise stacked expert weights W [E, rows, cols] (f32 or bf16), one dynamic
