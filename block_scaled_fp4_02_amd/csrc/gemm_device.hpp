@@ -348,13 +348,15 @@ __device__ __forceinline__ void swiglu_nvfp4_block(const float4v &gate, const fl
 
 // ---- launchers (one per kernel family) -------------------------------------------------
 
-enum Kernel { kLds = 0, kKSplit = 1, kRowMajor = 2, kLdsWide = 3 };
+enum Kernel { kLds = 0, kKSplit = 1, kRowMajor = 2, kLdsWide = 3, kLds64 = 4 };
 
 // Token tiles (16 rows) per work item of the packed-weight kernels.
 constexpr int kChunkTiles = 3;       // gemm_lds_kernel (4 waves, 256 weight rows)
+constexpr int kChunkTiles64 = 4;     // gemm_lds64_kernel (4 waves, 256 weight rows, 2 per CU)
 constexpr int kWideChunkTiles = 6;   // gemm_lds_wide_kernel (8 waves, 512 weight rows)
 
 void launch_lds(const Params &p, int epi, dim3 grid, hipStream_t stream);
+void launch_lds64(const Params &p, int epi, dim3 grid, hipStream_t stream);
 void launch_lds_wide(const Params &p, int epi, dim3 grid, hipStream_t stream);
 void launch_ksplit(const Params &p, int epi, int ks, dim3 grid, hipStream_t stream);
 int ksplit_chunk_rows();      // rows per work item of the K-split kernel

@@ -420,10 +420,15 @@ __device__ __forceinline__ void lds_k1_body(const Params &P, LdsShared<kChunkTil
 // LDS budget (lds_budget.hpp): the shared struct is exactly the budget entry, and the
 // workgroups the launch bounds promise per CU fit in its 160 KB.
 constexpr int kLdsWgPerCu = 3;
+constexpr int kLds64WgPerCu = 2;
 constexpr int kWideWgPerCu = 1;
 static_assert(sizeof(LdsShared<kChunkTiles, 4>) == lds::lds_kernel_bytes(kChunkTiles, 4),
               "LDS of the four-wave kernel differs from its budget entry");
 static_assert(lds::fits_cu(sizeof(LdsShared<kChunkTiles, 4>), kLdsWgPerCu), "four-wave tile exceeds the CU's LDS");
+static_assert(sizeof(LdsShared<kChunkTiles64, 4>) == lds::lds_kernel_bytes(kChunkTiles64, 4),
+              "LDS of the 64-row four-wave kernel differs from its budget entry");
+static_assert(lds::fits_cu(sizeof(LdsShared<kChunkTiles64, 4>), kLds64WgPerCu),
+              "64-row four-wave tile exceeds the CU's LDS");
 static_assert(sizeof(LdsShared<kWideChunkTiles, 8>) == lds::lds_kernel_bytes(kWideChunkTiles, 8),
               "LDS of the eight-wave kernel differs from its budget entry");
 static_assert(lds::fits_cu(sizeof(LdsShared<kWideChunkTiles, 8>), kWideWgPerCu), "eight-wave tile exceeds the CU's LDS");
@@ -464,6 +469,35 @@ __global__ __launch_bounds__(256, kLdsWgPerCu) void gemm_lds_kernel(Params P) {
   }
 }
 
+// About two work items per CU of tens of rows each (one 256-row n tile of each expert's
+// gate/up or down projection, e.g. 256 experts x 2 n tiles or 32 experts x 16): 64-row
+// chunks, so that every expert of up to 64 rows is a single item, and two workgroups per CU.
+// With 48-row chunks the few experts above 48 rows added a third item on some CUs, and
+// those CUs set the launch's duration.
+template <int EPI>
+__global__ __launch_bounds__(256, kLds64WgPerCu) void gemm_lds64_kernel(Params P) {
+  __shared__ LdsShared<kChunkTiles64, 4> sh;
+  const int b = blockIdx.x;
+  int4 item;
+  bool last;
+  if (!item_for_block(P, b, item, last)) {
+    if (EPI == MOE_EPI_SWIGLU && threadIdx.x == 0) P.amax_out[b] = 0.f;
+    return;
+  }
+  const int nm = (item.z + 15) / 16;   // workgroup-uniform
+  if (last) {
+    if (nm <= 1) lds_body<1, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
+    else if (nm == 2) lds_body<2, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
+    else if (nm == 3) lds_body<3, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
+    else lds_body<4, EPI, true>(P, sh, b, item.x, item.y, item.z, item.w);
+  } else {
+    if (nm <= 1) lds_body<1, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
+    else if (nm == 2) lds_body<2, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
+    else if (nm == 3) lds_body<3, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
+    else lds_body<4, EPI, false>(P, sh, b, item.x, item.y, item.z, item.w);
+  }
+}
+
 // Hundreds of rows per expert: eight waves share one activation tile of up to six token
 // tiles (96 rows), so each dequantised weight element serves twice as many tokens as in
 // gemm_lds_kernel, while two waves per SIMD (one workgroup of 512 threads per CU, 110,624
@@ -495,6 +529,14 @@ void launch_lds(const Params &p, int epi, dim3 grid, hipStream_t stream) {
   else if (epi == MOE_EPI_SWIGLU_NVFP4)
     hipLaunchKernelGGL(gemm_lds_kernel<MOE_EPI_SWIGLU_NVFP4>, grid, block, 0, stream, p);
   else hipLaunchKernelGGL(gemm_lds_kernel<MOE_EPI_NONE>, grid, block, 0, stream, p);
+}
+
+void launch_lds64(const Params &p, int epi, dim3 grid, hipStream_t stream) {
+  const dim3 block(256);
+  if (epi == MOE_EPI_SWIGLU) hipLaunchKernelGGL(gemm_lds64_kernel<MOE_EPI_SWIGLU>, grid, block, 0, stream, p);
+  else if (epi == MOE_EPI_SWIGLU_NVFP4)
+    hipLaunchKernelGGL(gemm_lds64_kernel<MOE_EPI_SWIGLU_NVFP4>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(gemm_lds64_kernel<MOE_EPI_NONE>, grid, block, 0, stream, p);
 }
 
 void launch_lds_wide(const Params &p, int epi, dim3 grid, hipStream_t stream) {

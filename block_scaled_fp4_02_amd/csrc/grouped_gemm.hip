@@ -21,6 +21,9 @@
 //  * Per-shape plan (the counterpart of the pages' tile table, chosen from host-known sizes
 //    only, so a supported launch cannot fail on its configuration):
 //      packed weights, >= 96 rows per expert       -> wide LDS kernel, 96-row chunks, 512-row n tiles
+//      packed weights, one item per (expert, n tile)
+//        filling two workgroups per CU, <= 40 rows
+//        per expert on average                     -> LDS kernel, 64-row chunks, 2 per CU
 //      packed weights, enough items for the chip   -> LDS kernel, 48-row chunks
 //      packed weights, few items (e.g. 8 groups)   -> K split 2/4/8 ways across a
 //                                                     workgroup's waves, 32-row chunks
@@ -161,6 +164,12 @@ GemmPlan plan_gemm(const moe_gemm_args &a) {
       p.kernel = kLdsWide;
       p.chunk_rows = kWideChunkTiles * 16;
       p.n_tile = 512;
+    } else if (a.K > kKStep && static_cast<int64_t>(a.E) * (a.N / 256) > 256 &&
+               static_cast<int64_t>(a.E) * (a.N / 256) <= 2 * 256 && a.R <= static_cast<int64_t>(a.E) * 40) {
+      // tens of rows per expert and one item per (expert, n tile) fills two workgroups per
+      // CU: 64-row chunks keep an expert of up to 64 rows in one item (two per CU)
+      p.kernel = kLds64;
+      p.chunk_rows = kChunkTiles64 * 16;
     } else if (a.K == kKStep && a.epilogue == MOE_EPI_NONE) {
       // one K step per item: several 256-row n tiles per item reuse the activation tile the
       // workgroup dequantised into LDS (the item's start-up -- lookup, row indices, activation
@@ -230,6 +239,7 @@ hipError_t launch_grouped_gemm(const moe_gemm_args &a, const GemmPlan &plan, voi
   switch (plan.kernel) {
     case kLds: launch_lds(p, a.epilogue, grid, stream); break;
     case kLdsWide: launch_lds_wide(p, a.epilogue, grid, stream); break;
+    case kLds64: launch_lds64(p, a.epilogue, grid, stream); break;
     case kKSplit: launch_ksplit(p, a.epilogue, plan.ks, grid, stream); break;
     default: launch_rowmajor(p, a.epilogue, plan.ks, grid, stream); break;
   }

@@ -104,6 +104,7 @@ struct TileEntry {
 
 constexpr TileEntry kTileTable[] = {
     {"decode LDS kernel (4 waves)", 48, 256, kKStepElems, 3, lds_kernel_bytes(3, 4)},
+    {"LDS kernel, 64-row chunks (4 waves)", 64, 256, kKStepElems, 2, lds_kernel_bytes(4, 4)},
     {"wide LDS kernel (8 waves)", 96, 512, kKStepElems, 1, lds_kernel_bytes(6, 8)},
     {"K split 2 ways (4 waves)", 32, 128, kKStepElems, 2, ksplit_kernel_bytes(2, 4)},
     {"K split 4 ways (4 waves)", 32, 64, kKStepElems, 2, ksplit_kernel_bytes(2, 4)},

@@ -151,6 +151,19 @@ def test_single_step_items_cover_several_n_tiles():
     assert slots(E=256, N=6144, K=512, R=8192) == bound_items(24)
 
 
+def test_plan_two_items_per_cu_uses_64_row_chunks():
+    """One item per (expert, n tile) filling two workgroups per CU at tens of rows per expert
+    (the TP8 and EP8 shares' gate/up GEMMs) takes 64-row chunks: the grid bound counts
+    n_tiles * (ceil(R / 64) + E) items; otherwise 48-row chunks."""
+    L = moe.lib()
+    slots = lambda **kw: L.moe_grouped_gemm_nvfp4_amax_slots(C.byref(gemm_args(layout=1, **kw)))
+    bound = lambda R, E, n_tiles, chunk: -(-(n_tiles * (-(-R // chunk) + E)) // 8) * 8
+    assert slots(E=256, N=512, K=6144, R=8192, epi=1) == bound(8192, 256, 2, 64)      # TP8 gate/up
+    assert slots(E=32, N=4096, K=6144, R=1024, epi=1) == bound(1024, 32, 16, 64)      # EP8 gate/up
+    assert slots(E=256, N=4096, K=6144, R=8192, epi=1) == bound(8192, 256, 16, 48)    # decode: many items
+    assert slots(E=256, N=512, K=6144, R=40 * 256 + 1, epi=1) == bound(40 * 256 + 1, 256, 2, 48)   # > 40 rows each
+
+
 def test_gemm_workspace_grows_with_rows_and_experts():
     """Launches whose items are looked up in the kernel need only the 16-byte item count (up
     to 64 experts, or up to 256 with K >= 1024 outside the K-split kernel); the others hold

@@ -272,6 +272,9 @@ def _run_gemm_none(A, Bs, off, A_rows, R, label, packed=False):
     # in the second case, an odd number of 256-wide K steps
     ([0, 1, 96, 127, 128, 129, 300, 513], 512, 512, True),
     ([100, 200, 57, 0], 768, 256, True),
+    # 32 experts x 16 n tiles with tens of rows each: the 64-row four-wave kernel (two items per
+    # CU), every token-tile count 1..4 and an expert of 65 rows (two chunks)
+    ([0, 1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 40, 20] + [30] * 16, 512, 4096, True),
     # >= 96 rows per expert and N % 512 == 0: the 8-wave kernel with 96-row chunks; the groups
     # end in every token-tile count 1..6
     ([1, 17, 33, 49, 65, 81, 95, 96, 97, 200, 600], 512, 512, True),
@@ -464,7 +467,9 @@ def _run_gemm_swiglu(A, Bs, off, A_rows, R, label, rows=None, packed=False):
                                        ([0, 130, 255, 97], 768, 256),    # several chunks, odd K steps
                                        ([20, 32], 2048, 256),            # K split 8 ways
                                        ([33] * 14, 2048, 1024),          # K split 8 ways, items looped
-                                       ([20, 32], 6144, 256)])           # K split 8 ways, 7 and 5 half steps
+                                       ([20, 32], 6144, 256),            # K split 8 ways, 7 and 5 half steps
+                                       # 256 experts x 2 n tiles, 0-65 rows each: the 64-row kernel
+                                       ([int(v) for v in np.random.default_rng(5).integers(0, 66, 256)], 512, 256)])
 def test_gemm_swiglu_shapes(sizes, K, I, packed):
     A, Bs, off, A_rows, R = _gemm_case(sizes, K, 2 * I, True, seed=7 + K + I)
     _run_gemm_swiglu(A, Bs, off, A_rows, R, f"sizes={sizes}", packed=packed)
@@ -475,7 +480,10 @@ def test_gemm_swiglu_shapes(sizes, K, I, packed):
                                              ([40] * 256 + [3, 0, 64], 256, 512, 1.0),   # LDS kernel
                                              ([20, 32], 2048, 256, 1.0),                 # K split 8 ways
                                              ([33] * 14, 2048, 1024, 1.0),               # K split, items looped
-                                             ([0, 130, 255, 97], 768, 256, 2.0)])        # 8-wave kernel
+                                             ([0, 130, 255, 97], 768, 256, 2.0),         # 8-wave kernel
+                                             # 256 experts x 2 n tiles, 0-65 rows: 64-row kernel
+                                             ([int(v) for v in np.random.default_rng(5).integers(0, 66, 256)],
+                                              512, 256, 1.0)])
 def test_gemm_swiglu_nvfp4_fused(sizes, K, I, g_div):
     """SwiGLU + NVFP4 epilogue with a static global scale g2: codes and scales equal the
     oracle's static-scale quantisation of the GPU's own SwiGLU output byte for byte (same

@@ -40,9 +40,10 @@ int main() {
            (long long)e.workgroups_per_cu, (long long)e.lds_bytes, e.name);
   printf("budget %lld %lld %lld\n", (long long)kSm120OptInBlockBytes, (long long)kSm120BytesPerSm,
          (long long)kCdna4BytesPerCu);
-  printf("lds %lld %lld ksplit %lld %lld rowmajor %lld %lld %lld\n", (long long)lds_kernel_bytes(3, 4),
+  printf("lds %lld %lld ksplit %lld %lld rowmajor %lld %lld %lld lds64 %lld\n", (long long)lds_kernel_bytes(3, 4),
          (long long)lds_kernel_bytes(6, 8), (long long)ksplit_kernel_bytes(2, 4), (long long)ksplit_kernel_bytes(2, 8),
-         (long long)rowmajor_kernel_bytes(1), (long long)rowmajor_kernel_bytes(2), (long long)rowmajor_kernel_bytes(4));
+         (long long)rowmajor_kernel_bytes(1), (long long)rowmajor_kernel_bytes(2), (long long)rowmajor_kernel_bytes(4),
+         (long long)lds_kernel_bytes(4, 4));
   return 0;
 }
 """
@@ -71,6 +72,7 @@ def probe(tmp_path_factory):
             rec["lds4"], rec["lds8"] = int(f[1]), int(f[2])
             rec["ksplit4"], rec["ksplit8"] = int(f[4]), int(f[5])
             rec["rowmajor"] = {1: int(f[7]), 2: int(f[8]), 4: int(f[9])}
+            rec["lds64"] = int(f[11])
     return rec
 
 
@@ -113,6 +115,7 @@ def test_plan_tiles_fit_cdna4(probe):
     assert probe["lds4"] == 49168 and probe["lds8"] == 110624
     assert probe["ksplit4"] == 32784 and probe["ksplit8"] == 65568
     assert probe["rowmajor"] == {1: 20, 2: 32784, 4: 49168}
+    assert probe["lds64"] == 65552
 
 
 # ---- what the compiler allocates ---------------------------------------------------
@@ -160,6 +163,8 @@ def test_compiled_kernels_within_budget(probe, tmp_path):
             entry, waves, waves_per_simd, fam = probe["lds8"], 8, 2, "wide"
         elif "gemm_lds_kernel" in name:
             entry, waves, waves_per_simd, fam = probe["lds4"], 4, 3, "lds"
+        elif "gemm_lds64_kernel" in name:
+            entry, waves, waves_per_simd, fam = probe["lds64"], 4, 2, "lds64"
         elif "gemm_ksplit_kernel" in name:
             ks = int(re.search(r"gemm_ksplit_kernelILi(\d+)E", name).group(1))
             entry, waves, waves_per_simd, fam = probe["ksplit8" if ks == 8 else "ksplit4"], max(4, ks), 2, "ksplit"
@@ -175,4 +180,4 @@ def test_compiled_kernels_within_budget(probe, tmp_path):
         assert u["lds"] * workgroups_per_cu <= 163840, (name, u)
         assert u["occupancy"] >= waves_per_simd, (name, u)
         assert u["scratch"] == 0, (name, u)   # no register spills
-    assert seen == {"wide", "lds", "ksplit", "rowmajor"}
+    assert seen == {"wide", "lds", "lds64", "ksplit", "rowmajor"}
