@@ -23,7 +23,10 @@
 //    non-temporal hint (no later item of the launch reads them again); earlier chunks keep
 //    them in L2 for the next chunk.
 // Chunks of up to 48 rows (three token tiles), 49,168 bytes of LDS and at most 168 VGPRs, so three
-// workgroups share a CU and overlap one another's loads, dequantisation and MFMAs.  Per step
+// workgroups share a CU and overlap one another's loads, dequantisation and MFMAs.  A second
+// four-wave kernel takes 64-row chunks (four tiles, 65,552 bytes, two workgroups per CU) for
+// launches of about two items per CU, where a 48-row chunk's remainder items would put a
+// third workgroup on some CUs; an eight-wave kernel shares 96-row chunks at prefill sizes.  Per step
 // and wave: 264 VALU (weight dequantisation) for 32*NM MFMAs.  At decode sizes the kernel
 // streams weights (HBM-bound); at hundreds of rows per expert it runs the same tile over
 // several chunks, whose repeated weight reads are adjacent items on one XCD and hit its L2.
