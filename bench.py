@@ -518,14 +518,19 @@ def run_layer(L, moe, torch, steps: int, warmup: int, weights=None, fused: bool 
     x_bytes = L.T * (L.H // 2 + L.H // 16)
     act_bytes = R * L.I * 2
     g1_alg_bytes = w1_bytes + x_bytes + act_bytes
+    # the down GEMM reads the requantised act and writes one bf16 row of H per routed row
+    # (at a small I, e.g. a tensor-parallel share, these writes are a large part of its bytes)
+    g2_alg_bytes = w2_bytes + R * (L.I // 2 + L.I // 16) + R * L.H * 2
     g1_s = stage_us["gemm1"] * 1e-6
     g2_s = stage_us["gemm2"] * 1e-6
     weight_gbps = (w1_bytes + w2_bytes) / (g1_s + g2_s) / 1e9
+    gemm_alg_gbps = (g1_alg_bytes + g2_alg_bytes) / (g1_s + g2_s) / 1e9
     return {"plan": plan, "weights": (W1, W2), "off": off, "sizes": sizes, "ms_per_step": ms_per_step,
             "graph_ms_per_step": graph_ms_per_step, "stage_us": stage_us,
             "value": (gemm1_flops + gemm2_flops) / (ms_per_step * 1e-3) / 1e12,
             "gemm_tflops": (gemm1_flops + gemm2_flops) / (g1_s + g2_s) / 1e12,
-            "weight_gbps": weight_gbps, "g1_alg_bytes": g1_alg_bytes, "g1_s": g1_s, "g1_flops": gemm1_flops}
+            "weight_gbps": weight_gbps, "gemm_alg_gbps": gemm_alg_gbps, "g1_alg_bytes": g1_alg_bytes,
+            "g2_alg_bytes": g2_alg_bytes, "g1_s": g1_s, "g1_flops": gemm1_flops}
 
 
 def roofline_record(L, r) -> dict:
@@ -560,6 +565,8 @@ def shard_record(L, moe, torch, steps: int, weights=None) -> dict:
            "graph_ms_per_step": round(r["graph_ms_per_step"], 4), "tflops": round(r["value"], 2),
            "gemm_tflops": round(r["gemm_tflops"], 2), "weight_hbm_GBps": round(r["weight_gbps"], 1),
            "weight_hbm_frac": round(r["weight_gbps"] / HBM_PEAK_GBPS, 4),
+           "gemm_alg_hbm_GBps": round(r["gemm_alg_gbps"], 1),
+           "gemm_alg_hbm_frac": round(r["gemm_alg_gbps"] / HBM_PEAK_GBPS, 4),
            "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
            "offsets": [int(v) for v in r["off"]]}
     del r
@@ -642,6 +649,8 @@ def main():
         "gemm_tflops": round(r["gemm_tflops"], 2),
         "weight_hbm_GBps": round(r["weight_gbps"], 1),
         "weight_hbm_frac": round(r["weight_gbps"] / HBM_PEAK_GBPS, 4),
+        "gemm_alg_hbm_GBps": round(r["gemm_alg_gbps"], 1),
+        "gemm_alg_hbm_frac": round(r["gemm_alg_gbps"] / HBM_PEAK_GBPS, 4),
         "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
     }
     off, row_src = r["off"], r["plan"].row_src.cpu().numpy()
