@@ -264,6 +264,10 @@ def _run_gemm_none(A, Bs, off, A_rows, R, label, packed=False):
     ([1] * 60 + [0, 40, 2] + [1] * 37, 512, 256, True),   # 100 experts, K split 2 ways: listed items looped
     ([0, 3, 17, 48, 49, 1] * 42 + [5, 0, 60, 2], 1024, 1024, True),  # 256 experts, four-wave kernel, in-kernel lookup
     ([96, 130, 0, 250, 97] * 40, 1024, 512, False),       # 200 experts, eight-wave kernel, in-kernel lookup
+    # expert counts that leave the in-kernel lookup's last lane part-filled (four experts per
+    # lane): 127 experts in the four-wave kernel, 101 in the eight-wave kernel
+    ([0, 3, 17, 48, 49, 1, 30] * 18 + [5], 1024, 1536, True),
+    ([96, 130, 0, 250, 97] * 20 + [150], 1024, 512, True),
     ([0, 1, 2, 3, 5, 8, 13] * 150 + [40, 0], 256, 256, True),  # 1052 experts: two scan blocks in the schedule
     ([0, 0, 0], 256, 256, False),                         # no rows at all
     ([300], 256, 768, True),                              # one big group: several row chunks
@@ -469,7 +473,9 @@ def _run_gemm_swiglu(A, Bs, off, A_rows, R, label, rows=None, packed=False):
                                        ([33] * 14, 2048, 1024),          # K split 8 ways, items looped
                                        ([20, 32], 6144, 256),            # K split 8 ways, 7 and 5 half steps
                                        # 256 experts x 2 n tiles, 0-65 rows each: the 64-row kernel
-                                       ([int(v) for v in np.random.default_rng(5).integers(0, 66, 256)], 512, 256)])
+                                       ([int(v) for v in np.random.default_rng(5).integers(0, 66, 256)], 512, 256),
+                                       # 131 experts at K 1024: in-kernel lookup, last lane part-filled
+                                       ([int(v) for v in np.random.default_rng(6).integers(0, 60, 131)], 1024, 768)])
 def test_gemm_swiglu_shapes(sizes, K, I, packed):
     A, Bs, off, A_rows, R = _gemm_case(sizes, K, 2 * I, True, seed=7 + K + I)
     _run_gemm_swiglu(A, Bs, off, A_rows, R, f"sizes={sizes}", packed=packed)
