@@ -131,17 +131,32 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 
 __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
+// A token's k expert ids are read kIdBatch at a time, every load of a batch issued before any
+// is used (indices past the token's last id re-read that id and are discarded): in a loop over
+// a run-time k each load would otherwise wait for the one before it.
+constexpr int kIdBatch = 8;
+
+__device__ __forceinline__ void load_id_batch(const int32_t *__restrict__ tok_ids, int k, int j0,
+                                              int32_t (&v)[kIdBatch]) {
+#pragma unroll
+  for (int u = 0; u < kIdBatch; u++) v[u] = tok_ids[min(j0 + u, k - 1)];
+}
+
 // Fill the chunk's per-expert token bitmaps (bm[e * kWords + w]).
-__device__ __forceinline__ void build_bitmaps(unsigned long long *bm, const int32_t *ids, int T,
+__device__ __forceinline__ void build_bitmaps(unsigned long long *bm, const int32_t *__restrict__ ids, int T,
                                               int E, int k, int chunk) {
   for (int i = threadIdx.x; i < E * kWords; i += blockDim.x) bm[i] = 0ull;
   __syncthreads();
   const int t = chunk * kChunk + threadIdx.x;
   if (t < T) {
     const unsigned long long bit = 1ull << (threadIdx.x & 63);
-    for (int j = 0; j < k; j++) {
-      const int e = clamp_expert(ids[static_cast<int64_t>(t) * k + j], E);
-      atomicOr(&bm[e * kWords + (threadIdx.x >> 6)], bit);
+    const int32_t *tok_ids = ids + static_cast<int64_t>(t) * k;
+    for (int j0 = 0; j0 < k; j0 += kIdBatch) {
+      int32_t v[kIdBatch];
+      load_id_batch(tok_ids, k, j0, v);
+#pragma unroll
+      for (int u = 0; u < kIdBatch; u++)
+        if (j0 + u < k) atomicOr(&bm[clamp_expert(v[u], E) * kWords + (threadIdx.x >> 6)], bit);
     }
   }
   __syncthreads();
@@ -242,14 +257,21 @@ __device__ __forceinline__ void scatter_chunk(const int32_t *__restrict__ ids, i
   const int word = threadIdx.x >> 6;
   const unsigned long long below = (1ull << (threadIdx.x & 63)) - 1ull;
   const int64_t n = static_cast<int64_t>(T) * k;
-  for (int j = 0; j < k; j++) {
-    const int e = clamp_expert(ids[static_cast<int64_t>(t) * k + j], E);
-    int rank = __popcll(bm[e * kWords + word] & below);
-    for (int w = 0; w < word; w++) rank += __popcll(bm[e * kWords + w]);
-    int64_t p = static_cast<int64_t>(base[e]) + rank;
-    p = p < 0 ? 0 : (p >= n ? n - 1 : p);
-    row_src[p] = t;
-    token_slot_row[static_cast<int64_t>(t) * k + j] = static_cast<int32_t>(p);
+  const int32_t *tok_ids = ids + static_cast<int64_t>(t) * k;
+  for (int j0 = 0; j0 < k; j0 += kIdBatch) {
+    int32_t v[kIdBatch];
+    load_id_batch(tok_ids, k, j0, v);
+#pragma unroll
+    for (int u = 0; u < kIdBatch; u++) {
+      if (j0 + u >= k) break;
+      const int e = clamp_expert(v[u], E);
+      int rank = __popcll(bm[e * kWords + word] & below);
+      for (int w = 0; w < word; w++) rank += __popcll(bm[e * kWords + w]);
+      int64_t p = static_cast<int64_t>(base[e]) + rank;
+      p = p < 0 ? 0 : (p >= n ? n - 1 : p);
+      row_src[p] = t;
+      token_slot_row[static_cast<int64_t>(t) * k + j0 + u] = static_cast<int32_t>(p);
+    }
   }
 }
 
