@@ -581,8 +581,13 @@ def test_layer_tiny_end_to_end(packed):
     check_bf16(got, r.out64, "layer tiny")
 
 
+# 131 experts (not a multiple of four) with K = 1024 in both GEMMs: every GEMM of the layer
+# looks its work items up in the kernel with the lookup's last lane part-filled
+LAYER_E131 = synth.Layer("layer_t512_e131_k8_h1024_i1024", T=512, E=131, k=8, H=1024, I=1024)
+
+
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("L", [synth.LAYER_DECODE, synth.LAYER_SKEWED, synth.LAYER_EP8, synth.LAYER_TP8],
+@pytest.mark.parametrize("L", [synth.LAYER_DECODE, synth.LAYER_SKEWED, synth.LAYER_EP8, synth.LAYER_TP8, LAYER_E131],
                          ids=lambda L: L.name)
 def test_layer_full_size_end_to_end(L):
     W1, W2, d1, d2 = layer_weights(L)
