@@ -488,8 +488,7 @@ def run_layer(L, moe, torch, steps: int, warmup: int, weights=None, fused: bool 
     torch.cuda.synchronize()
     stage_us = {st: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)]) * 1e3)
                 for i, st in enumerate(stages)}
-    # the timed steps: whole forward passes (routing and token quantisation overlap on two
-    # streams), bracketed by device synchronisation
+    # the timed steps: whole forward passes on one stream, bracketed by device synchronisation
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):

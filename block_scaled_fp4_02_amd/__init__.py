@@ -329,9 +329,6 @@ class MoELayerPlan:
         self.ws_q2 = _ws(L.moe_quantize_nvfp4_workspace(R, I), dev)
         self.ws_g1 = _ws(moe_grouped_gemm_nvfp4_workspace(self.args1), dev)
         self.ws_g2 = _ws(moe_grouped_gemm_nvfp4_workspace(self.args2), dev)
-        # routing reads the logits and the token quantiser reads x: independent, so forward()
-        # runs the quantiser on a second stream (default priority) beside the routing kernels
-        self.side = torch.cuda.Stream(device=dev)
 
     # the six calls of the layer, individually (the benchmark times them one by one)
     def route(self, logits, stream=None):
@@ -357,11 +354,12 @@ class MoELayerPlan:
         moe_finalize(self.Y, self.w, self.tsr, self.out, stream)
 
     def forward(self, logits, x, stream=None):
+        # One stream.  Routing (logits) and token quantisation (x) are independent, but running
+        # the quantiser on a second stream beside the routing kernels made the layer slower:
+        # the two cross-stream waits cost more than the ~15 us the overlap saves.
         main = stream if stream is not None else torch.cuda.current_stream()
-        self.side.wait_stream(main)          # logits and x are ready on the main stream
-        self.quantize_input(x, self.side)
         self.route(logits, main)
-        main.wait_stream(self.side)          # GEMM1 needs both
+        self.quantize_input(x, main)
         self.gemm1(main)
         self.requantize(main)
         self.gemm2(main)
@@ -369,8 +367,7 @@ class MoELayerPlan:
         return self.out
 
     def graph(self, logits, x) -> "torch.cuda.CUDAGraph":
-        """Capture one forward pass over the input buffers `logits` and `x` into a HIP graph
-        (both streams: the quantiser's branch forks from and joins the capture stream).
+        """Capture one forward pass over the input buffers `logits` and `x` into a HIP graph.
         replay() reruns the whole layer on whatever those buffers hold at the time, writing
         the same output buffers; a serving loop copies each batch into them first.  The pass
         allocates nothing and records no memory-set node: every buffer is cleared or written
