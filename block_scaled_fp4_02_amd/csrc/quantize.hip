@@ -14,7 +14,10 @@
 //
 // Two kernels: amax_kernel writes up to kAmaxParts partial maxima into the workspace;
 // quant_kernel (one thread per 16-element block) first reduces those partials itself
-// (order-free, so every workgroup sees the same g) and then quantises.  Memory-bound:
+// (order-free, so every workgroup sees the same g) and then quantises.  Up to
+// kDirectParts caller-provided maxima (e.g. a SwiGLU GEMM's partial maxima at a few hundred
+// workgroups) are reduced by quant_kernel directly, without the amax_kernel launch: at those
+// sizes the launch costs more than every workgroup reading the maxima.  Memory-bound:
 // reads 2 (bf16) or 4 (f32) bytes and writes 0.5625 bytes per element.
 #include "common.hpp"
 #include "nvfp4_round.hpp"
@@ -25,6 +28,7 @@ namespace moe {
 namespace {
 
 constexpr int kAmaxParts = 256;
+constexpr int kDirectParts = 1024;
 
 __device__ __forceinline__ float load_abs_max8_bf16(const uint4 v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -91,6 +95,8 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const void *__restri
   }
 }
 
+// PARTS: the most partial maxima the kernel reduces (64 lanes x PARTS / 64 loads each)
+template <int PARTS>
 __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, int x_dtype,
                                                     int64_t nblk, uint8_t *__restrict__ q,
                                                     uint8_t *__restrict__ sf, float *__restrict__ gs,
@@ -115,13 +121,16 @@ __global__ __launch_bounds__(256) void quant_kernel(const void *__restrict__ x, 
   if (threadIdx.x < 64) {
     float g;
     if (dynamic) {
-      // nparts <= kAmaxParts = 4 * 64: four loads per lane, all in flight at once (indices
-      // clamped to the last partial, which a maximum may read twice)
-      static_assert(kAmaxParts <= 4 * 64, "one round of loads covers the partial maxima");
-      float v[4];
+      // nparts <= PARTS: PARTS / 64 loads per lane, all in flight at once (indices clamped to
+      // the last partial, which a maximum may read twice)
+      constexpr int kPer = PARTS / 64;
+      static_assert(PARTS % 64 == 0, "whole loads per lane");
+      float v[kPer];
 #pragma unroll
-      for (int u = 0; u < 4; u++) v[u] = parts[min(static_cast<int>(threadIdx.x) + 64 * u, nparts - 1)];
-      float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+      for (int u = 0; u < kPer; u++) v[u] = parts[min(static_cast<int>(threadIdx.x) + 64 * u, nparts - 1)];
+      float m = 0.f;
+#pragma unroll
+      for (int u = 0; u < kPer; u++) m = fmaxf(m, fabsf(v[u]));
       m = wave_max(m);
       g = (m > 0.f) ? m / 2688.0f : 1.0f;  // 2688 = 6 * 448
       if (blockIdx.x == 0 && threadIdx.x == 0) *gs = g;
@@ -196,7 +205,9 @@ hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t C, 
   float *parts = static_cast<float *>(ws);
   const int dynamic = gs_mode == MOE_GS_DYNAMIC;
   int nparts = 0;
-  if (dynamic) {
+  // few caller-provided maxima: quant_kernel reduces them itself
+  const bool direct = dynamic && amax_in != nullptr && n_amax_in >= 1 && n_amax_in <= kDirectParts;
+  if (dynamic && !direct) {
     // partial maxima: ~4 per thread; tensor data: ~32 elements per thread
     const int64_t per_wg = kAmaxThreads * (amax_in ? 4 : 32);
     const int64_t g = ((amax_in ? n_amax_in : n) + per_wg - 1) / per_wg;
@@ -206,8 +217,12 @@ hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t C, 
   }
   if (nblk > 0 || dynamic) {
     const int64_t grid = nblk > 0 ? (nblk + 255) / 256 : 1;  // one block still publishes g
-    hipLaunchKernelGGL(quant_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, x,
-                       x_dtype, nblk, q, sf, gs, dynamic, parts, nparts);
+    if (direct)
+      hipLaunchKernelGGL(quant_kernel<kDirectParts>, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, x,
+                         x_dtype, nblk, q, sf, gs, dynamic, amax_in, static_cast<int>(n_amax_in));
+    else
+      hipLaunchKernelGGL(quant_kernel<kAmaxParts>, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, x,
+                         x_dtype, nblk, q, sf, gs, dynamic, parts, nparts);
   }
   return hipGetLastError();
 }

@@ -154,6 +154,20 @@ def test_quantize_static_and_partials():
     _check_quant(x, bf16=True, partials=parts)
 
 
+@pytest.mark.parametrize("n", [1, 63, 64, 997, 1024, 1025, 4096])
+@pytest.mark.parametrize("where", ["first", "last"])
+def test_quantize_partial_maxima_counts(n, where):
+    """Dynamic scale from n caller-provided maxima: up to 1024 the quantiser reduces them
+    itself (no partial-maxima launch), above it a reduction launch comes first; the largest
+    one first or last (the last lane's clamped loads), the others random and smaller."""
+    rng = np.random.default_rng(n)
+    x = synth.bf16_to_f32(synth.bf16_bits(rng.standard_normal((64, 512)).astype(np.float32)))
+    m = np.float32(np.abs(x).max())
+    parts = (rng.uniform(0, 1, n) * m * np.float32(0.9)).astype(np.float32)
+    parts[0 if where == "first" else n - 1] = m
+    _check_quant(x, bf16=True, partials=parts)
+
+
 @pytest.mark.parametrize("case", ["zeros", "tiny_block", "wide_range", "one_block", "negzero", "subnormal_dynamic",
                                   "subnormal_static"])
 def test_quantize_edges(case):
