@@ -552,7 +552,10 @@ def test_requantize_bit_exact_from_partials():
 # ---------------------------------------------------------------------------------------
 # FINALIZE
 
-@pytest.mark.parametrize("T,E,k,H", [(16, 4, 2, 256), (1024, 256, 8, 6144), (5, 3, 3, 8), (64, 32, 1, 512)])
+@pytest.mark.parametrize("T,E,k,H", [(16, 4, 2, 256), (1024, 256, 8, 6144), (5, 3, 3, 8), (64, 32, 1, 512),
+                                     (37, 64, 32, 264),    # k = 32, the largest the call takes
+                                     (3, 32, 32, 8),       # k = E = 32, one 8-column chunk
+                                     (9, 16, 4, 2056)])    # 257 column chunks: a second, ragged round of threads
 def test_finalize(T, E, k, H):
     log(f"finalize T={T} k={k} H={H}")
     rng = np.random.default_rng(T + H)
@@ -567,6 +570,17 @@ def test_finalize(T, E, k, H):
     got = host_bits(out)
     check_bf16(got, ref64, f"finalize T={T} k={k} H={H}")
     assert (got == np_bf16_round(ref64)).mean() > 0.99
+
+
+def test_finalize_no_tokens():
+    """T = 0: nothing to combine; the call succeeds and launches nothing (empty tensors)."""
+    Y = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    w = torch.empty(0, 2, dtype=torch.float32, device="cuda")
+    tsr = torch.empty(0, dtype=torch.int32, device="cuda")
+    out = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    moe.moe_finalize(Y, w, tsr, out)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
 
 
 # ---------------------------------------------------------------------------------------
