@@ -296,6 +296,8 @@ def _run_gemm_none(A, Bs, off, A_rows, R, label, packed=False):
     # >= 96 rows per expert and N % 512 == 0: the 8-wave kernel with 96-row chunks; the groups
     # end in every token-tile count 1..6
     ([1, 17, 33, 49, 65, 81, 95, 96, 97, 200, 600], 512, 512, True),
+    # the 8-wave kernel with a single K step (only the loop's odd-step tail runs)
+    ([96, 130, 200, 0, 60], 256, 1024, True),
 ])
 def test_gemm_none_shapes(sizes, K, N, gather, packed):
     A, Bs, off, A_rows, R = _gemm_case(sizes, K, N, gather, seed=sum(sizes) + K + N)
@@ -489,7 +491,9 @@ def _run_gemm_swiglu(A, Bs, off, A_rows, R, label, rows=None, packed=False):
                                        # 256 experts x 2 n tiles, 0-65 rows each: the 64-row kernel
                                        ([int(v) for v in np.random.default_rng(5).integers(0, 66, 256)], 512, 256),
                                        # 131 experts at K 1024: in-kernel lookup, last lane part-filled
-                                       ([int(v) for v in np.random.default_rng(6).integers(0, 60, 131)], 1024, 768)])
+                                       ([int(v) for v in np.random.default_rng(6).integers(0, 60, 131)], 1024, 768),
+                                       # 8-wave kernel, one K step
+                                       ([100, 150, 200, 3], 256, 256)])
 def test_gemm_swiglu_shapes(sizes, K, I, packed):
     A, Bs, off, A_rows, R = _gemm_case(sizes, K, 2 * I, True, seed=7 + K + I)
     _run_gemm_swiglu(A, Bs, off, A_rows, R, f"sizes={sizes}", packed=packed)
