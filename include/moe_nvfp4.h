@@ -123,8 +123,8 @@ moe_status moe_route_permute(const float *logits, int T, int E, int k, int32_t *
  * x_dtype: MOE_DTYPE_BF16 (x is uint16 bf16 bit patterns) or MOE_DTYPE_F32.
  * gs_mode MOE_GS_DYNAMIC: g = amax / 2688 in binary32 (1 if amax is 0), written
  *   to *gs; amax is max|x| over the whole tensor, or, when amax_in is not NULL,
- *   the maximum of the n_amax_in values amax_in[] (e.g. the partial maxima a
- *   SwiGLU GEMM wrote).
+ *   the maximum of |amax_in[i]| over its n_amax_in entries (e.g. the partial maxima
+ *   a SwiGLU GEMM wrote; 0 entries give amax 0).
  * gs_mode MOE_GS_STATIC: g is read from *gs.
  * Then per block b: t = amax_b / (6 g), s = e4m3(min(t, 448)) (round to nearest
  * even), and per element u = |x| / (s g), code = sign(x) | e2m1(min(u, 6))
